@@ -1,0 +1,183 @@
+"""ctypes binding of libsparse_attn.so: same names as the C ABI, argument marshalling only.
+
+Every computation happens in the HIP library.  If the library is missing the
+functions raise; there is no fallback path.
+"""
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
+
+SA_OK = 0
+SA_ERR_INVALID_ARGUMENT = -1
+SA_ERR_UNSUPPORTED = -2
+SA_ERR_CAPACITY = -3
+SA_ERR_EMPTY_ROW = -4
+SA_ERR_HIP = -5
+SA_BF16 = 0
+SA_F32 = 1
+SA_ORDER_IDENTITY = 0
+SA_ORDER_WINDOW = 1
+SA_ORDER_HILBERT = 2
+SA_PV_GROUP_ROWS = 32
+SA_MAX_KEY_BLOCKS = 2048
+
+EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermute",
+           "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
+           "sa_sparse_attn_fwd")
+
+
+class SaLayout(ctypes.Structure):
+    _fields_ = [("n_tokens", c_int64), ("order", c_int32), ("t", c_int32), ("h", c_int32),
+                ("w", c_int32), ("win_t", c_int32), ("win_h", c_int32), ("win_w", c_int32),
+                ("txt_len", c_int32), ("first_frame_sink", c_int32)]
+
+
+class SaMaskParams(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32), ("N", c_int64),
+                ("block_q", c_int32), ("block_k", c_int32), ("causal", c_int32),
+                ("reserved0", c_int32), ("window", c_int64), ("sink_front", c_int64),
+                ("sink_back", c_int64), ("tau", c_double), ("theta", c_double),
+                ("sparsity", c_double), ("scale", c_float), ("reserved1", c_int32)]
+
+
+class SaAttnParams(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32), ("Dv", c_int32),
+                ("block_q", c_int32), ("block_k", c_int32), ("causal", c_int32), ("N", c_int64),
+                ("lam", c_float), ("scale", c_float), ("col_cap", c_int64)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {sa_status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m image_dit_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.sa_status_string.argtypes = [c_int]
+    L.sa_status_string.restype = c_char_p
+    L.sa_plan_permutation.argtypes = [POINTER(SaLayout), POINTER(c_int32), c_int64]
+    L.sa_plan_permutation.restype = c_int
+    L.sa_permute.argtypes = [c_void_p, c_int, c_void_p, c_void_p, c_int32, c_int32, c_int64, c_int32, c_void_p]
+    L.sa_permute.restype = c_int
+    L.sa_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64, c_int32, c_void_p]
+    L.sa_unpermute.restype = c_int
+    L.sa_predict_workspace_bytes.argtypes = [POINTER(SaMaskParams)]
+    L.sa_predict_workspace_bytes.restype = c_size_t
+    L.sa_predict_workspace_offsets.argtypes = [POINTER(SaMaskParams), POINTER(c_int64)]
+    L.sa_predict_workspace_offsets.restype = c_int
+    L.sa_predict_mask.argtypes = [c_void_p, c_void_p, POINTER(SaMaskParams), c_void_p, c_size_t, c_void_p,
+                                  c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.sa_predict_mask.restype = c_int
+    L.sa_sparse_attn_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(SaAttnParams),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.sa_sparse_attn_fwd.restype = c_int
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return c_void_p(stream)
+    return c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != SA_OK:
+        raise SparseAttnError(code, where)
+
+
+def sa_status_string(code: int) -> str:
+    return lib().sa_status_string(code).decode()
+
+
+def make_layout(n_tokens, order=SA_ORDER_IDENTITY, latent=(1, 1, 1), window=(1, 1, 1), txt_len=0,
+                first_frame_sink=False) -> SaLayout:
+    t, h, w = latent
+    wt, wh, ww = window
+    return SaLayout(n_tokens, order, t, h, w, wt, wh, ww, txt_len, int(first_frame_sink))
+
+
+def sa_plan_permutation(layout: SaLayout) -> np.ndarray:
+    """Host-only planner: returns perm (int32 [N]) with perm[i] = original index at position i."""
+    perm = np.empty(layout.n_tokens, dtype=np.int32)
+    code = lib().sa_plan_permutation(ctypes.byref(layout), perm.ctypes.data_as(POINTER(c_int32)),
+                                     c_int64(layout.n_tokens))
+    _check(code, "sa_plan_permutation")
+    return perm
+
+
+def sa_permute(x, y, perm, stream=None):
+    """y[b,h,i,:] = bf16(x[b,h,perm[i],:]); x bf16 or fp32 [B,H,N,D]; y bf16 [B,H,N,D]."""
+    import torch
+    B, H, N, D = x.shape
+    dt = SA_F32 if x.dtype == torch.float32 else SA_BF16
+    code = lib().sa_permute(_ptr(x), dt, _ptr(y), _ptr(perm), B, H, N, D, _stream(stream))
+    _check(code, "sa_permute")
+
+
+def sa_unpermute(y, x, perm, stream=None):
+    """x[b,h,perm[i],:] = y[b,h,i,:]; fp32 [B,H,N,Dv]."""
+    B, H, N, Dv = y.shape
+    code = lib().sa_unpermute(_ptr(y), _ptr(x), _ptr(perm), B, H, N, Dv, _stream(stream))
+    _check(code, "sa_unpermute")
+
+
+def make_mask_params(B, Hq, Hkv, N, D, block_q, block_k, causal=False, window=0, sink_front=0,
+                     sink_back=0, tau=None, theta=None, sparsity=None, scale=0.0) -> SaMaskParams:
+    return SaMaskParams(B, Hq, Hkv, D, N, block_q, block_k, int(causal), 0, window, sink_front,
+                        sink_back, -1.0 if tau is None else tau, 0.0 if theta is None else theta,
+                        -1.0 if sparsity is None else sparsity, scale, 0)
+
+
+def make_attn_params(B, Hq, Hkv, N, D, block_q, block_k, causal=False, lam=None, scale=0.0,
+                     col_cap=0) -> SaAttnParams:
+    return SaAttnParams(B, Hq, Hkv, D, D, block_q, block_k, int(causal), N,
+                        float("-inf") if lam is None else lam, scale, col_cap)
+
+
+def sa_predict_workspace_bytes(p: SaMaskParams) -> int:
+    return int(lib().sa_predict_workspace_bytes(ctypes.byref(p)))
+
+
+def sa_predict_workspace_offsets(p: SaMaskParams):
+    off = (c_int64 * 6)()
+    _check(lib().sa_predict_workspace_offsets(ctypes.byref(p), off), "sa_predict_workspace_offsets")
+    return list(off)
+
+
+def sa_predict_mask(q, k, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mask_out=None, sim_q=None,
+                    sim_k=None, stream=None):
+    code = lib().sa_predict_mask(_ptr(q), _ptr(k), ctypes.byref(p), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(mask_out), _ptr(sim_q),
+                                 _ptr(sim_k), _ptr(dev_status), _stream(stream))
+    _check(code, "sa_predict_mask")
+
+
+def sa_sparse_attn_fwd(q, k, v, o, p: SaAttnParams, row_ptr, col_idx, dev_status, pv_skip=None,
+                       counters=None, stream=None):
+    code = lib().sa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), ctypes.byref(p), _ptr(row_ptr),
+                                    _ptr(col_idx), _ptr(pv_skip), _ptr(counters), _ptr(dev_status),
+                                    _stream(stream))
+    _check(code, "sa_sparse_attn_fwd")

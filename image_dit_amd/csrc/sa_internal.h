@@ -1,0 +1,85 @@
+// Internal declarations shared by the C-ABI layer and the kernel translation
+// units.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+// Geometry of one predict call, derived from sa_mask_params.
+struct PredictShape {
+    int B, Hq, Hkv, D;
+    int64_t N;
+    int bq, bk;
+    int64_t n_qb, n_kb;
+    int64_t rows;  // B * Hq * n_qb
+    int64_t off[6];
+    size_t bytes;
+};
+
+// Fills s from p; returns SA_OK or an error code.  Pure host arithmetic.
+int predict_shape(const sa_mask_params* p, PredictShape* s);
+int validate_predict(const sa_mask_params* p);
+int validate_attn(const sa_attn_params* p);
+
+// Kernel launchers (each enqueues on `stream`; returns hipError_t).
+hipError_t launch_permute(const void* x, int x_dtype, uint16_t* y, const int32_t* perm,
+                          int64_t rows_bh, int64_t N, int D, hipStream_t stream);
+hipError_t launch_unpermute(const float* y, float* x, const int32_t* perm, int64_t rows_bh,
+                            int64_t N, int Dv, hipStream_t stream);
+
+struct TopCdfArgs {
+    const float* qbar;
+    const float* kbar;
+    const float* simq;
+    const float* simk;
+    uint8_t* mask;
+    int32_t* counts;
+    int B, Hq, Hkv, D;
+    int64_t N;
+    int bq, bk;
+    int n_qb, n_kb;
+    int causal;
+    int64_t window, sink_front, sink_back;
+    float tau;       // < 0: unset
+    double tau_d;    // tau as given, for the >= 1 test
+    float theta;     // <= 0: off
+    double sparsity;  // < 0: unset
+    float scale;
+};
+
+hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const PredictShape& s,
+                              float* qbar, float* kbar, float* simq, float* simk,
+                              int32_t* dev_status, hipStream_t stream);
+hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream);
+hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, int64_t rows, int n_kb,
+                      int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                      int32_t* dev_status, hipStream_t stream);
+
+struct FlashArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    float* o;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    uint8_t* pv_skip;
+    unsigned long long* counters;
+    int32_t* dev_status;
+    int B, Hq, Hkv, D;
+    int64_t N;
+    int bq, bk;
+    int n_qb, n_kb;
+    int64_t col_cap;
+    int causal;
+    float lambda;  // -inf: off
+    float scale;
+};
+
+hipError_t launch_flash(const FlashArgs& a, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,146 @@
+"""One call of the whole path: reorder -> predict mask -> sparse attention -> inverse reorder.
+
+Torch only allocates device memory and supplies the stream; every step runs
+in the HIP library through the C ABI (``_lib``).
+"""
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import _lib as L
+
+
+@dataclass
+class PathConfig:
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    D: int
+    block_q: int
+    block_k: int
+    order: int = L.SA_ORDER_IDENTITY
+    latent: Tuple[int, int, int] = (1, 1, 1)
+    window: Tuple[int, int, int] = (1, 1, 1)
+    txt_len: int = 0
+    first_frame_sink: bool = False
+    causal: bool = False
+    window_tokens: int = 0
+    sink_front: int = 0
+    sink_back: int = 0
+    tau: Optional[float] = None
+    theta: Optional[float] = None
+    sparsity: Optional[float] = None
+    lam: Optional[float] = None
+    scale: float = 0.0
+
+    @property
+    def n_qb(self):
+        return -(-self.N // self.block_q)
+
+    @property
+    def n_kb(self):
+        return -(-self.N // self.block_k)
+
+    @property
+    def rows(self):
+        return self.B * self.Hq * self.n_qb
+
+    def mask_params(self):
+        return L.make_mask_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
+                                  self.causal, self.window_tokens, self.sink_front, self.sink_back,
+                                  self.tau, self.theta, self.sparsity, self.scale)
+
+    def attn_params(self, col_cap=0):
+        return L.make_attn_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
+                                  self.causal, self.lam, self.scale, col_cap)
+
+    def layout(self):
+        return L.make_layout(self.N, self.order, self.latent, self.window, self.txt_len, self.first_frame_sink)
+
+
+def config_from_workload(w, sparsity="default") -> PathConfig:
+    """PathConfig from a workloads.Workload (duck-typed: no import of the oracle side)."""
+    return PathConfig(B=w.B, Hq=w.Hq, Hkv=w.Hkv, N=w.N, D=w.D, block_q=w.block_q, block_k=w.block_k,
+                      order=w.order, latent=w.latent, window=w.window, txt_len=w.txt_len,
+                      first_frame_sink=w.first_frame_sink, causal=w.causal, window_tokens=w.window_tokens,
+                      sink_front=w.sink_front, sink_back=w.sink_back, tau=w.tau, theta=w.theta,
+                      sparsity=w.sparsity if sparsity == "default" else sparsity, lam=w.lam)
+
+
+class SparseAttentionPath:
+    """Owns the device buffers of one workload shape and runs the four entry points."""
+
+    def __init__(self, cfg: PathConfig, device="cuda", col_cap: Optional[int] = None, want_skip=True):
+        import torch
+
+        self.cfg = cfg
+        self.device = device
+        self.perm_host = L.sa_plan_permutation(cfg.layout())
+        self.perm = torch.from_numpy(self.perm_host).to(device)
+        bf = torch.bfloat16
+        B, Hq, Hkv, N, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.D
+        self.qp = torch.empty((B, Hq, N, D), dtype=bf, device=device)
+        self.kp = torch.empty((B, Hkv, N, D), dtype=bf, device=device)
+        self.vp = torch.empty((B, Hkv, N, D), dtype=bf, device=device)
+        self.mp = cfg.mask_params()
+        ws_bytes = L.sa_predict_workspace_bytes(self.mp)
+        if ws_bytes == 0:
+            raise L.SparseAttnError(L.SA_ERR_INVALID_ARGUMENT, "sa_predict_workspace_bytes")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.ws_off = L.sa_predict_workspace_offsets(self.mp)
+        self.col_cap = cfg.rows * cfg.n_kb if col_cap is None else col_cap
+        self.ap = cfg.attn_params(self.col_cap)
+        self.row_ptr = torch.empty(cfg.rows + 1, dtype=torch.int32, device=device)
+        self.col_idx = torch.empty(max(self.col_cap, 1), dtype=torch.int32, device=device)
+        self.status = torch.zeros(2, dtype=torch.int32, device=device)
+        self.groups = -(-cfg.block_q // L.SA_PV_GROUP_ROWS)
+        self.pv_skip = (torch.empty(max(self.col_cap, 1) * self.groups, dtype=torch.uint8, device=device)
+                        if want_skip else None)
+        self.counters = torch.zeros(3, dtype=torch.int64, device=device)
+        self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
+        self.o = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
+
+    # --- the four steps (each one C-ABI call, or three for the permute) ---
+    def permute(self, q, k, v, stream=None):
+        L.sa_permute(q, self.qp, self.perm, stream)
+        L.sa_permute(k, self.kp, self.perm, stream)
+        L.sa_permute(v, self.vp, self.perm, stream)
+
+    def predict(self, mask_out=None, sim_q=None, sim_k=None, stream=None):
+        L.sa_predict_mask(self.qp, self.kp, self.mp, self.ws, self.row_ptr, self.col_idx[:self.col_cap]
+                          if self.col_cap > 0 else self.col_idx[:0], self.status[0:1], mask_out, sim_q, sim_k,
+                          stream)
+
+    def attend(self, stream=None):
+        L.sa_sparse_attn_fwd(self.qp, self.kp, self.vp, self.o_perm, self.ap, self.row_ptr, self.col_idx,
+                             self.status[1:2], self.pv_skip, self.counters, stream)
+
+    def unpermute(self, stream=None):
+        L.sa_unpermute(self.o_perm, self.o, self.perm, stream)
+
+    def run(self, q, k, v, stream=None):
+        self.permute(q, k, v, stream)
+        self.predict(stream=stream)
+        self.attend(stream)
+        self.unpermute(stream)
+        return self.o
+
+    # --- inspection helpers (host copies, for tests and reports) ---
+    def workspace_view(self, idx, dtype, shape):
+        import torch
+        start = self.ws_off[idx]
+        nbytes = int(np.prod(shape)) * torch.empty(0, dtype=dtype).element_size()
+        return self.ws[start:start + nbytes].view(dtype).view(*shape)
+
+    def csr_host(self):
+        rp = self.row_ptr.cpu().numpy().astype(np.int64)
+        nnz = int(rp[-1])
+        ci = self.col_idx[:min(nnz, self.col_cap)].cpu().numpy().astype(np.int64)
+        return rp, ci
+
+    def statuses(self):
+        s = self.status.cpu().numpy()
+        return int(s[0]), int(s[1])

@@ -1,0 +1,216 @@
+/*
+ * sparse_attn.h -- C ABI of the block-sparse attention forward library for
+ * AMD MI355X (gfx950): token reorder, block-mask prediction, sparse
+ * FlashAttention-style forward, inverse reorder.
+ *
+ * What is computed (sources cited by page title and section):
+ *   - Attention restricted to a kept key set is the softmax over the kept keys
+ *     only ("AIGC 基本功|视频稀疏注意力的误差与布局-SparseAttn", section 3.1);
+ *     reordering Q, K, V and both mask axes together and undoing the reorder on
+ *     the output leaves the operator unchanged (same article, section 3.4).
+ *   - Block-mask prediction from mean-pooled block representatives, a
+ *     self-similarity guard theta, a compressed softmax and TopCdf selection
+ *     at cumulative mass tau ("SpargeAttention: 中文精读笔记", section 2.2),
+ *     with first-frame / text sink blocks, a [t,h,w]-window or Hilbert token
+ *     reorder and a sparsity keep floor (MindIE-SD "稀疏" page: rf_v2 and the
+ *     sparse_attention interface; SpargeAttn notes, section 2.5), and a causal
+ *     sliding window ("44. Local Sliding and Sparse Attention", Step 2).
+ *   - Online-softmax attention over the kept (query block, key block) pairs,
+ *     skipping QK^T and PV for dropped blocks, and optionally skipping PV for a
+ *     group of query rows when the running-max gap is below lambda
+ *     (SpargeAttn notes, sections 2.1 and 2.3).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are contiguous BNSD: [batch, heads, tokens, head_dim], row-major,
+ *     with 16-byte aligned base pointers.  bf16 tensors are passed as uint16_t
+ *     bit patterns.
+ *   - Device pointers are owned by the caller.  The library never allocates,
+ *     frees or keeps device memory, never synchronizes, and enqueues work only
+ *     on the caller's stream (`stream` is a hipStream_t; NULL = the default
+ *     stream).  There is no global mutable state: calls are reentrant.
+ *   - Inputs are read-only; outputs are fully overwritten.
+ *   - Return value: SA_OK, or a negative SA_ERR_* code.  Argument checks are
+ *     done synchronously on the host before anything is enqueued, and never
+ *     touch the HIP runtime, so they also work on a machine without a GPU.
+ *     Conditions only visible on the device are written to the caller's
+ *     `dev_status` word (device memory, int32), which the call resets to
+ *     SA_OK first; read it after synchronizing.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define SA_OK                    0
+#define SA_ERR_INVALID_ARGUMENT (-1) /* bad shape, pointer or parameter */
+#define SA_ERR_UNSUPPORTED      (-2) /* head dim or block-size pair not compiled */
+#define SA_ERR_CAPACITY         (-3) /* col_idx too small (device status) */
+#define SA_ERR_EMPTY_ROW        (-4) /* a query block keeps no key block (device status) */
+#define SA_ERR_HIP              (-5) /* a HIP launch failed */
+
+/* ---- element types accepted by sa_permute ---------------------------- */
+#define SA_BF16 0
+#define SA_F32  1
+
+/* ---- token orders for sa_plan_permutation ---------------------------- */
+#define SA_ORDER_IDENTITY 0
+#define SA_ORDER_WINDOW   1
+#define SA_ORDER_HILBERT  2
+
+/* Query rows that share one PV-skip decision: the rows of one wavefront. */
+#define SA_PV_GROUP_ROWS 32
+
+/* Largest number of key blocks per query block the mask predictor handles. */
+#define SA_MAX_KEY_BLOCKS 2048
+
+/* Token layout of one sequence (MindIE-SD "稀疏" page, sparse_attention
+ * arguments txt_len and latent_shape [t,h,w]).  In the original order the
+ * txt_len text tokens come first, then the t*h*w video tokens frame by frame
+ * in raster order. */
+typedef struct sa_layout {
+    int64_t n_tokens;         /* N; must equal txt_len + t*h*w unless order is IDENTITY */
+    int32_t order;            /* SA_ORDER_* */
+    int32_t t, h, w;          /* latent grid of the video tokens */
+    int32_t win_t, win_h, win_w; /* reorder window, SA_ORDER_WINDOW only */
+    int32_t txt_len;          /* text tokens (prepended in the original order) */
+    int32_t first_frame_sink; /* 1: frame 0 stays first, in raster order */
+} sa_layout;
+
+/* Block-mask prediction parameters (SpargeAttn notes, sections 2.1-2.2;
+ * MindIE-SD sparse_attention arguments). */
+typedef struct sa_mask_params {
+    int32_t B, Hq, Hkv;       /* batch, query heads, key/value heads (Hq % Hkv == 0) */
+    int32_t D;                /* head dim: 64 or 128 */
+    int64_t N;                /* tokens per sequence */
+    int32_t block_q, block_k; /* b_q, b_k (tokens per query / key block), 1..256 */
+    int32_t causal;           /* 0 or 1 */
+    int32_t reserved0;        /* must be 0 */
+    int64_t window;           /* causal sliding window W in tokens (0 = off; needs causal) */
+    int64_t sink_front;       /* key blocks touching tokens [0, sink_front) are always kept */
+    int64_t sink_back;        /* key blocks touching tokens [N-sink_back, N) are always kept */
+    double tau;               /* TopCdf mass in (0, 1]; negative = unset */
+    double theta;             /* self-similarity guard; <= 0 = off */
+    double sparsity;          /* keep floor: ceil((1-s)*|valid|) blocks per row, s in [0,1); negative = unset */
+    float scale;              /* score scale; 0 = 1/sqrt(D) */
+    int32_t reserved1;        /* must be 0 */
+} sa_mask_params;
+
+/* Sparse attention parameters (SpargeAttn notes, section 2.1 table). */
+typedef struct sa_attn_params {
+    int32_t B, Hq, Hkv;
+    int32_t D, Dv;            /* D == Dv, 64 or 128 */
+    int32_t block_q, block_k; /* compiled pairs: (16,16), (128,64), (128,128) */
+    int32_t causal;
+    int64_t N;
+    float lambda;             /* PV-skip threshold (< 0); -INFINITY = off */
+    float scale;              /* 0 = 1/sqrt(D) */
+    int64_t col_cap;          /* entries col_idx holds; CSR entries at or past it are not read */
+} sa_attn_params;
+
+/* Static text for a status code.  Never NULL. */
+const char* sa_status_string(int code);
+
+/* Host only.  Token reorder (MindIE-SD "稀疏" page, rf_v2 window reorder and
+ * first-frame sink; SpargeAttn notes, section 2.5, Hilbert order).
+ *   perm_host[i] = original index of the token placed at position i.
+ * IDENTITY: perm = 0..N-1.  Otherwise frame 0 comes first in raster order when
+ * first_frame_sink is set; the remaining frames follow in window order
+ * (window t, h, w, then t, h, w inside a window, all raster) or Hilbert order
+ * (J. Skilling's transform on the enclosing 2^k cube, axis 0 = t most
+ * significant); the text tokens come last, in their original order.
+ * n must equal L->n_tokens.  Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
+int sa_plan_permutation(const sa_layout* L, int32_t* perm_host, int64_t n);
+
+/* Row gather with conversion to bf16 (SparseAttn article, section 3.4):
+ *   y[b,h,i,:] = bf16_round_nearest_even(x[b,h,perm[i],:])
+ * x: device [B,H,N,D] of x_dtype (SA_BF16 or SA_F32); y: device bf16 [B,H,N,D];
+ * perm_dev: device int32 [N], a permutation of 0..N-1 (not checked).
+ * D must be a multiple of 8.  With the identity permutation this is the
+ * documented way to hand fp32 inputs to the bf16 kernels.  x and y must not
+ * overlap. */
+int sa_permute(const void* x, int x_dtype, uint16_t* y, const int32_t* perm_dev,
+               int32_t B, int32_t H, int64_t N, int32_t D, void* stream);
+
+/* Inverse row scatter (SparseAttn article, section 3.4):
+ *   x[b,h,perm[i],:] = y[b,h,i,:]
+ * y, x: device fp32 [B,H,N,Dv] (no overlap); perm_dev: device int32 [N]. */
+int sa_unpermute(const float* y, float* x, const int32_t* perm_dev,
+                 int32_t B, int32_t H, int64_t N, int32_t Dv, void* stream);
+
+/* Bytes of device workspace sa_predict_mask needs for these parameters
+ * (block means and similarities, the dense block mask, row counts), or 0 when
+ * the parameters are invalid. */
+size_t sa_predict_workspace_bytes(const sa_mask_params* p);
+
+/* Byte offsets inside the workspace, for inspection after a call:
+ * off[0] query-block means fp32 [B,Hq,n_qb,D]; off[1] key-block means fp32
+ * [B,Hkv,n_kb,D]; off[2] query-block similarity fp32 [B,Hq,n_qb];
+ * off[3] key-block similarity fp32 [B,Hkv,n_kb]; off[4] block mask uint8
+ * [B,Hq,n_qb,n_kb]; off[5] kept blocks per row int32 [B*Hq*n_qb].
+ * Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
+int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
+
+/* Block-mask prediction on the PERMUTED q (device bf16 [B,Hq,N,D]) and k
+ * (device bf16 [B,Hkv,N,D]) (SpargeAttn notes, section 2.2; MindIE-SD rf_v2).
+ * Per (batch b, query head h, query block i), with n_qb = ceil(N/b_q),
+ * n_kb = ceil(N/b_k), KV head h / (Hq/Hkv):
+ *   1. block means and similarity ||mean_t x_t/||x_t||||^2 over the block's real tokens;
+ *   2. valid key blocks: all, or (causal) those whose first token is not after
+ *      the query block's last token;
+ *   3. forced key blocks (within the valid set): key similarity < theta; sink
+ *      blocks; causal: window blocks (last key >= first query - W + 1) and the
+ *      blocks overlapping the query block;
+ *   4. query similarity < theta: the whole valid row is kept;
+ *   5. otherwise the other valid blocks are candidates: scores
+ *      qbar.kbar*scale, softmax over the candidates, sorted by probability
+ *      descending then block index ascending; TopCdf keeps the blocks whose
+ *      preceding mass is still < tau (tau unset: none); the keep floor adds
+ *      blocks up to ceil((1-s)*|valid|) kept in total (s unset: none);
+ *   6. row = forced + kept.
+ * Outputs: row_ptr device int32 [B*Hq*n_qb + 1] and col_idx device int32
+ * [col_cap], the CSR of kept key blocks per row, rows in (b, h, i) order, each
+ * row ascending.  When the total exceeds col_cap, col_idx keeps the first
+ * col_cap entries and dev_status is set to SA_ERR_CAPACITY (row_ptr is still
+ * the full count).  Optional (NULL = not written): mask_out device uint8
+ * [B,Hq,n_qb,n_kb] (1 = kept), sim_q device fp32 [B,Hq,n_qb], sim_k device fp32
+ * [B,Hkv,n_kb].  ws: device workspace of ws_bytes >= sa_predict_workspace_bytes(p),
+ * 256-byte aligned.  n_kb must not exceed SA_MAX_KEY_BLOCKS. */
+int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* p,
+                    void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
+                    int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
+                    int32_t* dev_status, void* stream);
+
+/* Sparse attention forward over the CSR of kept key blocks (SpargeAttn notes,
+ * section 2.1: online softmax m, l, O; section 2.3: PV skip).
+ * q device bf16 [B,Hq,N,D], k and v device bf16 [B,Hkv,N,D] (permuted order),
+ * o device fp32 [B,Hq,N,Dv].  row_ptr/col_idx as written by sa_predict_mask
+ * (any CSR with ascending in-range columns is accepted).  For each query row:
+ * the keys of its kept blocks (causal: only keys at or before it), softmax
+ * with scores q.k*scale, output sum p v.  Key blocks are visited in ascending
+ * order; with lambda set, for each group of SA_PV_GROUP_ROWS rows of a query
+ * block, if max over the group of (block row max - new running max) < lambda,
+ * the block's PV product is skipped for the group (the running sum still
+ * counts it).  A row that keeps no key gets NaN and dev_status is set to
+ * SA_ERR_EMPTY_ROW.  CSR entries at positions >= p->col_cap are ignored and
+ * set SA_ERR_CAPACITY; a column outside [0, n_kb) is ignored and sets
+ * SA_ERR_INVALID_ARGUMENT.
+ * Optional (NULL = not written): pv_skip device uint8 [nnz * ceil(block_q/32)]
+ * (G = ceil(block_q/32) flags per CSR entry, col_cap entries)
+ * with pv_skip[e*G + g] = 1 when group g skipped the PV of CSR entry e;
+ * counters device int64 [3] = {QK block products, PV group-blocks executed,
+ * PV group-blocks skipped}, reset by the call. */
+int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
+                       const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
+                       uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

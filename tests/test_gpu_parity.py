@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle (MI355X only).
+
+Reduced-size versions of the five workloads (several tiles, ragged tails),
+checked step by step: permutation (bit-exact), block statistics, predicted
+mask (exact except oracle-flagged borderline rows), CSR (bit-exact against
+the GPU's own mask), attention outputs on the GPU's CSR (max-abs 1e-2,
+mean-abs 1e-3 against fp64), PV-skip decisions and counters.
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import image_dit_amd as sa  # noqa: E402
+from oracle import attention as OA  # noqa: E402
+from oracle import layout as OL  # noqa: E402
+from oracle import numerics as ON  # noqa: E402
+from oracle import predict as OP  # noqa: E402
+from workloads import CONFIGS, generate  # noqa: E402
+
+import _ref as R  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+rep = dataclasses.replace
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "image_s": rep(CONFIGS["image"], Hq=3, Hkv=3, latent=(1, 20, 37)),
+    "video_s": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20,
+                   sink_front=16 * 24, sink_back=20),
+    "long_video_s": rep(CONFIGS["long_video"], Hq=2, Hkv=2, latent=(6, 10, 21)),
+    "long_video_d64": rep(CONFIGS["long_video"], Hq=2, Hkv=2, latent=(5, 9, 23), D=64, seed=41),
+    "causal_s": rep(CONFIGS["causal_long"], Hq=4, Hkv=2, latent=(1, 1, 2000), window_tokens=512),
+    "causal_s64": rep(CONFIGS["causal_long"], Hq=2, Hkv=1, latent=(1, 1, 777), window_tokens=300,
+                      block_k=64, seed=51),
+}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x: np.ndarray):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_path(w, sparsity="default"):
+    cfg = sa.config_from_workload(w, sparsity)
+    path = sa.SparseAttentionPath(cfg)
+    q, k, v = generate(w)
+    mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
+    simq = torch.zeros(cfg.rows, dtype=torch.float32, device="cuda")
+    simk = torch.zeros(cfg.B * cfg.Hkv * cfg.n_kb, dtype=torch.float32, device="cuda")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    path.permute(qd, kd, vd)
+    path.predict(mask_out=mask, sim_q=simq, sim_k=simk)
+    path.attend()
+    path.unpermute()
+    torch.cuda.synchronize()
+    return path, (q, k, v), mask.cpu().numpy().astype(bool), simq.cpu().numpy(), simk.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_path_parity(name):
+    w = SMALL[name]
+    log(f"[parity] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k}")
+    path, (q, k, v), gmask, gsimq, gsimk = run_path(w)
+    cfg = path.cfg
+    st_pred, st_attn = path.statuses()
+    assert st_pred == sa.SA_OK and st_attn == sa.SA_OK
+
+    # (a1) permutation: planner and gathered rows, bit-exact
+    perm = R.oracle_perm(w)
+    assert np.array_equal(path.perm_host.astype(np.int64), perm)
+    want_q = ON.f32_to_bf16(q) if q.dtype == np.float32 else q
+    assert np.array_equal(host_bits(path.qp), np.take(want_q, perm, axis=2))
+    want_v = ON.f32_to_bf16(v) if v.dtype == np.float32 else v
+    assert np.array_equal(host_bits(path.vp), np.take(want_v, perm, axis=2))
+
+    qp = R.permuted(q, perm)
+    kp = R.permuted(k, perm)
+    vp = R.permuted(v, perm)
+    G = w.Hq // w.Hkv
+    mp = R.mask_params(w)
+    qbar_g = path.workspace_view(0, torch.float32, (cfg.B, cfg.Hq, cfg.n_qb, cfg.D)).cpu().numpy()
+    kbar_g = path.workspace_view(1, torch.float32, (cfg.B, cfg.Hkv, cfg.n_kb, cfg.D)).cpu().numpy()
+    rp, ci = path.csr_host()
+    o_perm = path.o_perm.cpu().numpy()
+    skip = path.pv_skip.cpu().numpy() if path.pv_skip is not None else None
+    groups = path.groups
+
+    n_bad = n_border = n_rows = 0
+    errs_max, errs_sum, errs_n = 0.0, 0.0, 0
+    lam_far = lam_diff = 0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = h // G
+            ref = OP.predict_head(qp[b, h], kp[b, hk], mp)
+            # (a2) block statistics
+            r0 = (b * w.Hq + h) * cfg.n_qb
+            assert np.allclose(qbar_g[b, h], ref["qbar"], rtol=1e-5, atol=1e-5)
+            assert np.allclose(kbar_g[b, hk], ref["kbar"], rtol=1e-5, atol=1e-5)
+            assert np.allclose(gsimq[r0:r0 + cfg.n_qb], ref["simq"], rtol=1e-5, atol=1e-5)
+            kb0 = (b * w.Hkv + hk) * cfg.n_kb
+            assert np.allclose(gsimk[kb0:kb0 + cfg.n_kb], ref["simk"], rtol=1e-5, atol=1e-5)
+            # (a3) predicted mask
+            bad, border, checked = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref)
+            n_bad += len(bad)
+            n_border += len(border)
+            n_rows += checked
+            for i in border:  # a borderline row keeps its forced blocks and differs by at most a swap
+                if "theta" in ref["info"][i]["border"]:
+                    continue
+                forced = OP._forced_blocks(i, mp, ref["simk"], OP._valid_blocks(i, mp))
+                assert np.all(gmask[r0 + i][forced])
+                assert np.count_nonzero(gmask[r0 + i] != ref["mask"][i]) <= 2
+            # (a5) attention on the GPU's CSR, PV decisions replayed
+            ys, recs = R.attend_rows(qp[b, h], kp[b, hk], vp[b, hk], w, rp, ci, r0, range(cfg.n_qb),
+                                     skip, groups)
+            for i, y in ys.items():
+                got = o_perm[b, h, i * w.block_q:i * w.block_q + y.shape[0]]
+                d = np.abs(got - y)
+                errs_max = max(errs_max, float(d.max()))
+                errs_sum += float(d.sum())
+                errs_n += d.size
+                if w.lam is not None:
+                    f, dd = R.lambda_disagreements(recs[i], w.lam)
+                    lam_far += f
+                    lam_diff += dd
+    log(f"[parity] {name}: rows={n_rows} mask_mismatch={n_bad} borderline={n_border} "
+        f"out_max={errs_max:.3e} out_mean={errs_sum / errs_n:.3e} lam_diff={lam_diff} lam_far={lam_far}")
+    assert n_bad == 0
+    assert errs_max <= R.MAX_ABS and errs_sum / errs_n <= R.MEAN_ABS
+    assert lam_far == 0
+
+    # (a4) CSR is exactly the GPU mask, rows ascending
+    rp_m, ci_m = OP.mask_to_csr(gmask)
+    assert np.array_equal(rp, rp_m) and np.array_equal(ci, ci_m)
+
+    # counters: QK blocks = nnz; PV decisions of real groups add up; skips = bits set
+    cnt = path.counters.cpu().numpy()
+    nnz = int(rp[-1])
+    assert cnt[0] == nnz
+    real_groups = 0
+    skipped = 0
+    for r in range(cfg.rows):
+        i = r % cfg.n_qb
+        ng = -(-(min((i + 1) * w.block_q, w.N) - i * w.block_q) // 32)
+        real_groups += ng * (rp[r + 1] - rp[r])
+        if skip is not None:
+            for e in range(rp[r], rp[r + 1]):
+                skipped += int(skip[e * groups:e * groups + ng].sum())
+    assert cnt[1] + cnt[2] == real_groups
+    if skip is not None:
+        assert cnt[2] == skipped
+    if w.lam is None:
+        assert cnt[2] == 0
+
+    # (a6) unpermute is the exact inverse scatter
+    o = path.o.cpu().numpy()
+    assert np.array_equal(o, OL.unpermute_rows(o_perm, perm))
+
+
+def test_dense_when_sparsity_zero():
+    """Sparsity 0 keeps every block: the output is dense attention (all-ones mask)."""
+    w = rep(SMALL["image_s"], tau=None, sparsity=0.0, Hq=2, Hkv=2)
+    path, (q, k, v), gmask, _, _ = run_path(w)
+    assert gmask.all()
+    perm = R.oracle_perm(w)
+    o = path.o.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hq):
+            y, _ = OA.dense_attention(R.to_f64(q[b, h]), R.to_f64(k[b, h]), R.to_f64(v[b, h]))
+            d = np.abs(o[b, h] - y)
+            assert d.max() <= R.MAX_ABS and d.mean() <= R.MEAN_ABS
+
+
+def test_permute_fp32_round_to_nearest_even():
+    rng = np.random.default_rng(3)
+    N, D = 333, 64
+    x = (rng.normal(size=(2, 3, N, D)) * 50).astype(np.float32)
+    bits = x.view(np.uint32)
+    bits[0, 0, :, :8] = (bits[0, 0, :, :8] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)  # exact ties
+    perm = rng.permutation(N).astype(np.int32)
+    y = torch.empty((2, 3, N, D), dtype=torch.bfloat16, device="cuda")
+    sa.sa_permute(dev(x), y, torch.from_numpy(perm).cuda())
+    torch.cuda.synchronize()
+    want = np.take(ON.f32_to_bf16(x), perm, axis=2)
+    assert np.array_equal(host_bits(y), want)
+    back = torch.empty((2, 3, N, D), dtype=torch.float32, device="cuda")
+    yf = dev(ON.bf16_to_f64(want).astype(np.float32))
+    sa.sa_unpermute(yf, back, torch.from_numpy(perm).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), OL.unpermute_rows(ON.bf16_to_f64(want).astype(np.float32), perm))
+
+
+def test_empty_row_gives_nan_and_status():
+    w = rep(SMALL["long_video_s"], lam=None)
+    cfg = sa.config_from_workload(w)
+    path = sa.SparseAttentionPath(cfg)
+    q, k, v = generate(w)
+    path.permute(dev(q), dev(k), dev(v))
+    rows, n_kb = cfg.rows, cfg.n_kb
+    rp = np.zeros(rows + 1, dtype=np.int32)
+    cols = []
+    for r in range(rows):
+        c = [] if r == 3 else [0, r % n_kb] if r % n_kb else [0]
+        cols += c
+        rp[r + 1] = len(cols)
+    path.row_ptr.copy_(torch.from_numpy(rp))
+    path.col_idx[:len(cols)].copy_(torch.from_numpy(np.array(cols, dtype=np.int32)))
+    path.attend()
+    torch.cuda.synchronize()
+    assert path.statuses()[1] == sa.SA_ERR_EMPTY_ROW
+    o = path.o_perm.cpu().numpy()
+    i = 3 % cfg.n_qb
+    blk = o[0, 3 // cfg.n_qb, i * 128:(i + 1) * 128]
+    assert np.isnan(blk).all()
+    assert np.isfinite(o[0, 0, :128]).all()
+
+
+def test_capacity_overflow_sets_status():
+    w = SMALL["image_s"]
+    cfg = sa.config_from_workload(w)
+    full = sa.SparseAttentionPath(cfg)
+    q, k, v = generate(w)
+    full.permute(dev(q), dev(k), dev(v))
+    full.predict()
+    torch.cuda.synchronize()
+    rp, ci = full.csr_host()
+    cap = int(rp[-1]) // 2
+    small = sa.SparseAttentionPath(cfg, col_cap=cap)
+    small.permute(dev(q), dev(k), dev(v))
+    small.predict()
+    torch.cuda.synchronize()
+    assert small.statuses()[0] == sa.SA_ERR_CAPACITY
+    rp2, ci2 = small.csr_host()
+    assert np.array_equal(rp2, rp) and np.array_equal(ci2, ci[:cap])
+
+
+def test_rerun_is_bitwise_deterministic():
+    w = SMALL["long_video_s"]
+    cfg = sa.config_from_workload(w)
+    path = sa.SparseAttentionPath(cfg)
+    q, k, v = (dev(x) for x in generate(w))
+    outs = []
+    for _ in range(2):
+        path.run(q, k, v)
+        torch.cuda.synchronize()
+        rp, ci = path.csr_host()
+        outs.append((rp, ci, path.o.cpu().numpy().copy(), path.pv_skip.cpu().numpy().copy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32))
+    assert np.array_equal(outs[0][3], outs[1][3])

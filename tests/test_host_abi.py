@@ -1,0 +1,191 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* the library loads and exports every function include/sparse_attn.h declares;
+* the C++ planner (sa_plan_permutation) matches the oracle's independent
+  planner bit for bit;
+* invalid arguments are rejected synchronously, before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import image_dit_amd as sa
+from oracle import layout as Lay
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sa.LIB_PATH), reason="library not built")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(sa.EXPORTS)
+    L = sa.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    nm = os.popen(f"nm -D --defined-only {sa.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert sa.sa_status_string(code) and sa.sa_status_string(code) != "unknown status"
+    assert sa.sa_status_string(17) == "unknown status"
+
+
+def _layouts():
+    out = []
+    for w in CONFIGS.values():
+        out.append((w.N, w.order, w.latent, w.window, w.txt_len, w.first_frame_sink))
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        t, h, w = (int(x) for x in rng.integers(1, 9, size=3))
+        txt = int(rng.integers(0, 5))
+        win = tuple(int(x) for x in rng.integers(1, 5, size=3))
+        sink = bool(rng.integers(0, 2))
+        order = int(rng.integers(1, 3))
+        out.append((txt + t * h * w, order, (t, h, w), win, txt, sink))
+    out.append((4 * 4 * 4, Lay.ORDER_WINDOW, (4, 4, 4), (4, 1, 1), 0, False))
+    out.append((1 * 1 * 1, Lay.ORDER_HILBERT, (1, 1, 1), (1, 1, 1), 0, False))
+    out.append((17 * 1 * 40 + 3, Lay.ORDER_HILBERT, (17, 1, 40), (1, 1, 1), 3, True))
+    return out
+
+
+@pytest.mark.parametrize("case", range(len(_layouts())))
+def test_planner_matches_oracle(case):
+    N, order, latent, window, txt, sink = _layouts()[case]
+    got = sa.sa_plan_permutation(sa.make_layout(N, order, latent, window, txt, sink))
+    want = Lay.plan_permutation(N, order, latent, window, txt, sink)
+    assert got.dtype == np.int32
+    assert np.array_equal(got.astype(np.int64), want)
+
+
+def test_planner_rejects_bad_layouts():
+    bad = [sa.make_layout(10, sa.SA_ORDER_WINDOW, (2, 2, 2), (1, 1, 1), 1),   # 1 + 8 != 10
+           sa.make_layout(8, sa.SA_ORDER_WINDOW, (2, 2, 2), (0, 1, 1)),        # zero window
+           sa.make_layout(8, 7, (2, 2, 2)),                                    # unknown order
+           sa.make_layout(0, sa.SA_ORDER_IDENTITY)]
+    for lay in bad:
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sa_plan_permutation(lay)
+        assert e.value.code == sa.SA_ERR_INVALID_ARGUMENT
+    perm = np.empty(8, dtype=np.int32)
+    lay = sa.make_layout(8, sa.SA_ORDER_IDENTITY)
+    code = sa.lib().sa_plan_permutation(ctypes.byref(lay), perm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 7)
+    assert code == sa.SA_ERR_INVALID_ARGUMENT
+
+
+# -------------------------------------------------------------- validation (no device work)
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every case below fails validation
+
+
+def _mask_params(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64, tau=0.9)
+    base.update(kw)
+    return sa.make_mask_params(**base)
+
+
+def _predict_code(p, ws_bytes=1 << 30, **ptrs):
+    args = dict(q=FAKE, k=FAKE, ws=FAKE, row_ptr=FAKE, col_idx=FAKE, status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_predict_mask(args["q"], args["k"], ctypes.byref(p), args["ws"], ws_bytes,
+                                    args["row_ptr"], args["col_idx"], 100, None, None, None,
+                                    args["status"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=3, Hkv=2), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(block_q=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(block_k=300), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(tau=1.5), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(tau=0.0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(tau=None, sparsity=None), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(sparsity=1.0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(window=64), sa.SA_ERR_INVALID_ARGUMENT),           # window needs causal
+    (dict(causal=True, window=-1), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(sink_front=1001), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(theta=2.0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(D=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(N=4096 * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),  # more key blocks than supported
+])
+def test_predict_rejects_invalid_parameters(kw, code):
+    p = _mask_params(**kw)
+    assert sa.sa_predict_workspace_bytes(p) == 0
+    assert _predict_code(p) == code
+
+
+def test_predict_rejects_bad_buffers():
+    p = _mask_params()
+    need = sa.sa_predict_workspace_bytes(p)
+    assert need > 0
+    assert _predict_code(p, ws_bytes=need - 1) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_code(p, q=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_code(p, status=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_code(p, ws=ctypes.c_void_p((1 << 20) + 16)) == sa.SA_ERR_INVALID_ARGUMENT  # not 256-aligned
+    assert _predict_code(p, k=ctypes.c_void_p((1 << 20) + 2)) == sa.SA_ERR_INVALID_ARGUMENT    # not 16-aligned
+
+
+def test_workspace_layout():
+    p = _mask_params(B=2, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64)
+    off = sa.sa_predict_workspace_offsets(p)
+    n_qb, n_kb = 8, 16
+    sizes = [2 * 4 * n_qb * 128 * 4, 2 * 2 * n_kb * 128 * 4, 2 * 4 * n_qb * 4, 2 * 2 * n_kb * 4,
+             2 * 4 * n_qb * n_kb, 2 * 4 * n_qb * 4]
+    for i in range(6):
+        assert off[i] % 256 == 0
+        end = off[i] + sizes[i]
+        nxt = off[i + 1] if i < 5 else sa.sa_predict_workspace_bytes(p)
+        assert end <= nxt
+
+
+def _attn_code(p, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, row_ptr=FAKE, col_idx=FAKE, status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_sparse_attn_fwd(args["q"], args["k"], args["v"], args["o"], ctypes.byref(p),
+                                       args["row_ptr"], args["col_idx"], None, None, args["status"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=5, Hkv=2), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(lam=0.5), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(lam=float("nan")), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(D=32), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_q=64, block_k=64), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_q=128, block_k=32), sa.SA_ERR_UNSUPPORTED),
+])
+def test_attn_rejects_invalid_parameters(kw, code):
+    base = dict(B=1, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64)
+    base.update(kw)
+    assert _attn_code(sa.make_attn_params(**base)) == code
+
+
+def test_attn_rejects_bad_buffers():
+    p = sa.make_attn_params(1, 4, 2, 1000, 128, 128, 64)
+    assert _attn_code(p, v=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _attn_code(p, o=ctypes.c_void_p((1 << 20) + 4)) == sa.SA_ERR_INVALID_ARGUMENT
+
+
+def test_permute_rejects_invalid_arguments():
+    L = sa.lib()
+    assert L.sa_permute(FAKE, sa.SA_BF16, FAKE, FAKE, 1, 1, 10, 12, None) == sa.SA_ERR_INVALID_ARGUMENT  # D % 8
+    assert L.sa_permute(FAKE, 7, FAKE, FAKE, 1, 1, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert L.sa_permute(None, sa.SA_BF16, FAKE, FAKE, 1, 1, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert L.sa_unpermute(FAKE, FAKE, FAKE, 1, 0, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
