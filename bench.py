@@ -1,0 +1,307 @@
+"""Benchmark of the block-sparse attention forward path on one MI355X.
+
+A step is one pass of the whole path over one batch: reorder Q, K, V,
+predict the block mask, sparse attention, inverse reorder of the output.
+Default workload: the long-video shape (B=1, 24 heads, latent [28,30,53] ->
+N=44520, d=128, Hilbert order, b_q=128 / b_k=64, tau=0.95, theta=0.6,
+lambda=-8) at sparsity 0.8.  Inputs are synthetic, seeded, and resident in
+HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is executed TFLOP/s of the whole step
+(executed QK + PV flops of the sparse attention over the step time);
+``roofline`` covers the sparse attention kernel (bf16 MFMA bound);
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload (rank 0, N=1 only).
+
+Extra modes (for counter collection under rocprofv3, not for the JSON line):
+  --mode attn   only the sparse attention launch, repeated
+  --mode copy   a plain device copy of known size (HBM counter calibration)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "block-sparse attn fwd: ms/call + executed TFLOP/s (MFMA %) at sparsity 0.8"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_traffic_long_video.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_video")
+    ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
+    ap.add_argument("--mode", default="path", choices=["path", "attn", "copy"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def flash_source_hash():
+    h = hashlib.sha256()
+    for f in ("flash.hip", "sa_internal.h"):
+        with open(os.path.join(ROOT, "image_dit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def executed_flops(cfg, rp, ci, skip, groups):
+    """Executed QK and PV flops at real token counts, from the CSR and the PV-skip flags."""
+    import numpy as np
+
+    N, bq, bk, d = cfg.N, cfg.block_q, cfg.block_k, cfg.D
+    rows = len(rp) - 1
+    i = np.arange(rows) % cfg.n_qb
+    qrows = np.minimum((i + 1) * bq, N) - i * bq
+    cnt = np.diff(rp)
+    kcols = np.minimum((ci + 1) * bk, N) - ci * bk          # tokens per kept key block
+    row_of = np.repeat(np.arange(rows), cnt)
+    qk = 2.0 * float(np.sum(qrows[row_of] * kcols)) * d
+    pv = 0.0
+    for g in range(groups):
+        grow = np.clip(qrows - g * 32, 0, 32)[row_of]          # rows of group g in each entry's q-block
+        done = grow * kcols
+        if skip is not None and cfg.lam is not None:
+            done = done * (1 - skip[np.arange(len(ci)) * groups + g])
+        pv += 2.0 * float(np.sum(done)) * d
+    return qk, pv
+
+
+def cpu_baseline(w, path, q, k, v, budget_s):
+    """Oracle on a bounded sample: prediction of one head + attention of the first query blocks."""
+    import numpy as np
+
+    from oracle import flash as OF
+    from oracle import layout as OL
+    from oracle import numerics as ON
+    from oracle import predict as OP
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = path.cfg
+    h = 0
+    perm = OL.plan_permutation(w.N, w.order, w.latent, w.window, w.txt_len, w.first_frame_sink)
+    qp = OL.permute_rows(ON.bf16_to_f64(q[0, h]), perm)
+    kp = OL.permute_rows(ON.bf16_to_f64(k[0, h]), perm)
+    vp = OL.permute_rows(ON.bf16_to_f64(v[0, h]), perm)
+    mp = OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal, window=w.window_tokens,
+                       sink_front=w.sink_front, sink_back=w.sink_back, tau=w.tau, theta=w.theta,
+                       sparsity=cfg.sparsity)
+    t0 = time.perf_counter()
+    OP.predict_head(qp, kp, mp)
+    t_pred = time.perf_counter() - t0
+    rp, ci = path.csr_host()
+    t0 = time.perf_counter()
+    flops = 0.0
+    nblk = 0
+    while nblk < cfg.n_qb and (time.perf_counter() - t0) < budget_s:
+        cols = ci[rp[nblk]:rp[nblk + 1]]
+        _, rec = OF.attend_qblock(qp, kp, vp, nblk, cols, w.block_q, w.block_k, causal=w.causal,
+                                  lam=w.lam if w.lam is not None else None)
+        rows = min((nblk + 1) * w.block_q, w.N) - nblk * w.block_q
+        kts = np.array([min((j + 1) * w.block_k, w.N) - j * w.block_k for j in cols], dtype=np.float64)
+        flops += 2.0 * rows * kts.sum() * w.D  # QK
+        for g in range(rec["skip"].shape[1]):
+            grows = min(OF.PV_GROUP_ROWS, rows - g * OF.PV_GROUP_ROWS)
+            flops += 2.0 * grows * float(kts[~rec["skip"][:, g]].sum()) * w.D  # PV of executed groups
+        nblk += 1
+    t_attn = time.perf_counter() - t0
+    # per-head prediction cost is shared by the head's n_qb query blocks
+    t_pred_share = t_pred * nblk / cfg.n_qb
+    value = flops / (t_attn + t_pred_share) / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"head 0: block stats + mask prediction of all {cfg.n_qb} query blocks "
+                       f"({t_pred:.2f} s, charged pro rata) and fp64 attention with PV-skip emulation "
+                       f"on the first {nblk} query blocks over the GPU's CSR ({t_attn:.2f} s)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over heads with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import image_dit_amd as sa
+    from workloads import CONFIGS, generate
+
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
+        return
+
+    w = CONFIGS[args.workload]
+    if args.sparsity is not None:
+        w = w.with_sparsity(args.sparsity)
+    cfg = sa.config_from_workload(w)
+    path = sa.SparseAttentionPath(cfg)
+    t_gen = time.perf_counter()
+    q, k, v = generate(w)
+    t_gen = time.perf_counter() - t_gen
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    torch.cuda.synchronize()
+
+    if args.mode == "attn":
+        path.run(qd, kd, vd)
+        for _ in range(max(1, args.steps)):
+            path.attend()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "attn", "launches": max(1, args.steps) + 1}))
+        return
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        path.run(qd, kd, vd)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        path.permute(qd, kd, vd)
+        e[1].record(stream)
+        path.predict()
+        e[2].record(stream)
+        path.attend()
+        e[3].record(stream)
+        path.unpermute()
+        e[4].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    stage = np.zeros(4)
+    for e in ev:
+        for j in range(4):
+            stage[j] += e[j].elapsed_time(e[j + 1])
+    stage /= K
+    ms_step = total_ms / K
+
+    st = path.statuses()
+    if st != (sa.SA_OK, sa.SA_OK):
+        raise RuntimeError(f"device status {st}")
+    rp, ci = path.csr_host()
+    skip = path.pv_skip.cpu().numpy() if path.pv_skip is not None else None
+    qk, pv = executed_flops(cfg, rp, ci, skip, path.groups)
+    exec_flops = qk + pv
+    N, d, B, Hq, Hkv = cfg.N, cfg.D, cfg.B, cfg.Hq, cfg.Hkv
+    dense_flops = 4.0 * B * Hq * N * N * d if not cfg.causal else 4.0 * B * Hq * d * N * (N + 1) / 2
+    # combined QK+PV skipped fraction (block products), SpargeAttn notes section 3.2 "Sparsity"
+    cnt = path.counters.cpu().numpy()
+    nnz = int(rp[-1])
+    ib = np.arange(cfg.rows) % cfg.n_qb
+    if cfg.causal:
+        valid_blocks = np.minimum(cfg.n_kb, (np.minimum((ib + 1) * cfg.block_q, N) - 1) // cfg.block_k + 1)
+    else:
+        valid_blocks = np.full(cfg.rows, cfg.n_kb)
+    mask_sparsity = 1.0 - nnz / float(valid_blocks.sum())
+    pv_groups_total = cnt[1] + cnt[2]
+    combined = 1.0 - (nnz + cnt[1] * (nnz / max(1, pv_groups_total))) / (2.0 * valid_blocks.sum())
+
+    attn_ms = stage[2]
+    attn_tflops = exec_flops / (attn_ms * 1e-3) / 1e12
+    n_qb, n_kb = cfg.n_qb, cfg.n_kb
+    pred_bytes = (2 * (B * Hq * N * d + B * Hkv * N * d) + 4 * (B * Hq * n_qb + B * Hkv * n_kb) * d
+                  + 4 * (B * Hq * n_qb + B * Hkv * n_kb) + 2 * B * Hq * n_qb * n_kb
+                  + 4 * (B * Hq * n_qb + 1) + 4 * nnz)
+    perm_bytes = (B * Hq * N * d + 2 * B * Hkv * N * d) * ((4 if w.dtype == "f32" else 2) + 2)
+    unperm_bytes = 2 * 4 * B * Hq * N * d
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE, encoding="utf8") as f:
+            tr = json.load(f)
+        if tr.get("source_sha") == flash_source_hash() and tr.get("workload") == args.workload \
+                and abs(tr.get("sparsity", -1) - (cfg.sparsity or 0)) < 1e-9:
+            traffic = tr["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(exec_flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: B{B} Hq{Hq} Hkv{Hkv} latent{list(w.latent)} txt{w.txt_len} N{N} d{d} "
+                         f"order{w.order} bq{cfg.block_q} bk{cfg.block_k} tau{w.tau} theta{w.theta} "
+                         f"lambda{w.lam} sparsity{cfg.sparsity}"),
+            "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "block_q": cfg.block_q, "block_k": cfg.block_k,
+            "sparsity_target": cfg.sparsity,
+        },
+        "ms": {"permute": round(stage[0], 4), "predict": round(stage[1], 4), "attn": round(attn_ms, 4),
+               "unpermute": round(stage[3], 4)},
+        "attn_executed_tflops": round(attn_tflops, 2),
+        "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_equiv_tflops_step": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
+        "dense_equiv_tflops_attn_plus_predict": round(dense_flops / ((attn_ms + stage[1]) * 1e-3) / 1e12, 2),
+        "executed_tflop": round(exec_flops / 1e12, 4),
+        "dense_tflop": round(dense_flops / 1e12, 4),
+        "mask_sparsity": round(mask_sparsity, 4),
+        "combined_qk_pv_sparsity": round(float(combined), 4),
+        "pv_group_blocks": {"executed": int(cnt[1]), "skipped": int(cnt[2])},
+        "predict_gbs": round(pred_bytes / (stage[1] * 1e-3) / 1e9, 1),
+        "predict_hbm_frac": round(pred_bytes / (stage[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "permute_gbs": round(perm_bytes / (stage[0] * 1e-3) / 1e9, 1),
+        "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_flash_mfma (+ k_attn_init), per sa_sparse_attn_fwd call",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "wall_s_timed": round(t_wall, 3),
+        "gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, path, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

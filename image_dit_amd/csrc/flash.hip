@@ -245,6 +245,272 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     }
 }
 
+// Pipelined variant for 64-key tiles.  Each CSR entry covers SUB consecutive
+// 64-key tiles (SUB = 2 runs 128-key blocks as two online-softmax steps,
+// which is exact when no PV-skip decision needs the whole 128 keys).
+// K and V^T tiles are double-buffered in LDS: the global loads of tile t+1
+// are issued into registers before tile t is computed and written to the
+// other LDS buffer afterwards, so one barrier per tile suffices and the load
+// latency hides behind the MFMA/softmax work of this and the co-resident
+// workgroup.  Workgroups are mapped so that each XCD (workgroup id mod 8)
+// walks a contiguous range of (head, query block) rows: the K/V of the few
+// heads an XCD works on stay in its L2 and in the shared last-level cache.
+template <int D, int SUB, bool LAM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_flash_pipe(FlashArgs a) {
+    constexpr int BQ = 128;
+    constexpr int BK = 64;
+    constexpr int KSTR = D + 8;
+    constexpr int VSTR = BK + 4;
+    constexpr int NT = D / 32;
+    constexpr int KS = D / 16;
+    constexpr int KCH = D / 8;                      // 16-byte chunks per K row
+    constexpr int KL = BK * KCH / 256;              // K chunks per thread
+    constexpr int DB4 = D / 4;
+    constexpr int VL = (BK / 4) * DB4 / 256;        // 4x4 V blocks per thread
+    __shared__ __align__(16) uint16_t Ks[2][BK * KSTR];
+    __shared__ __align__(16) uint16_t Vt[2][D * VSTR];
+
+    const int G = a.B * a.Hq * a.n_qb;
+    const int per = (G + 7) >> 3;
+    const int row = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (row >= G) return;
+    const int qb = row % a.n_qb;
+    const int bh = row / a.n_qb;
+    const int hq = bh % a.Hq;
+    const int b = bh / a.Hq;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int N = int(a.N);
+    const uint16_t* Qh = a.q + int64_t(bh) * N * D;
+    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * N * D;
+    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * N * D;
+    float* Oh = a.o + int64_t(bh) * N * D;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int wrow0 = qb * BQ + wave * 32;
+    const int qrow = wrow0 + l32;
+    const bool row_valid = qrow < N;
+    const bool wave_rows = wrow0 < N;
+
+    bf16x8_t qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_valid) u = *reinterpret_cast<const uint4*>(Qh + int64_t(qrow) * D + ks * 16 + half * 8);
+        qf[ks] = as_bf16x8(u);
+    }
+
+    // per-thread staging geometry (fixed for the whole kernel)
+    int k_r[KL], k_c[KL], v_k[VL], v_d[VL];
+#pragma unroll
+    for (int c = 0; c < KL; ++c) {
+        const int idx = tid + 256 * c;
+        k_r[c] = idx / KCH;
+        k_c[c] = idx % KCH;
+    }
+#pragma unroll
+    for (int c = 0; c < VL; ++c) {
+        const int idx = tid + 256 * c;
+        v_k[c] = idx / DB4;
+        v_d[c] = idx % DB4;
+    }
+    uint4 kreg[KL];
+    uint2 vreg[VL][4];
+
+    const int e0 = a.row_ptr[row];
+    int e1 = a.row_ptr[row + 1];
+    if (e1 > a.col_cap) {
+        if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
+        e1 = int(a.col_cap);
+    }
+    const int nt = (e1 > e0 ? e1 - e0 : 0) * SUB;  // 64-key tiles to visit
+
+    // tile index t -> first key (or -1 for an out-of-range column)
+    auto tile_key0 = [&](int t) -> int {
+        const int j = a.col_idx[e0 + t / SUB];
+        if (j < 0 || j >= a.n_kb) return -1;
+        return j * (BK * SUB) + (t % SUB) * BK;
+    };
+    auto load_tile = [&](int kb0) {
+#pragma unroll
+        for (int c = 0; c < KL; ++c) {
+            const int key = kb0 + k_r[c];
+            kreg[c] = (kb0 >= 0 && key < N)
+                          ? *reinterpret_cast<const uint4*>(Kh + int64_t(key) * D + k_c[c] * 8)
+                          : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < VL; ++c)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int key = kb0 + v_k[c] * 4 + rr;
+                vreg[c][rr] = (kb0 >= 0 && key < N)
+                                  ? *reinterpret_cast<const uint2*>(Vh + int64_t(key) * D + v_d[c] * 4)
+                                  : make_uint2(0, 0);
+            }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < KL; ++c)
+            *reinterpret_cast<uint4*>(&Ks[buf][k_r[c] * KSTR + k_c[c] * 8]) = kreg[c];
+#pragma unroll
+        for (int c = 0; c < VL; ++c)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int sh = (cc & 1) * 16;
+                const uint32_t x0 = ((cc < 2 ? vreg[c][0].x : vreg[c][0].y) >> sh) & 0xffffu;
+                const uint32_t x1 = ((cc < 2 ? vreg[c][1].x : vreg[c][1].y) >> sh) & 0xffffu;
+                const uint32_t x2 = ((cc < 2 ? vreg[c][2].x : vreg[c][2].y) >> sh) & 0xffffu;
+                const uint32_t x3 = ((cc < 2 ? vreg[c][3].x : vreg[c][3].y) >> sh) & 0xffffu;
+                *reinterpret_cast<uint2*>(&Vt[buf][(v_d[c] * 4 + cc) * VSTR + v_k[c] * 4]) =
+                    make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+            }
+    };
+
+    floatx16 oacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
+    float m_run = -INFINITY;  // running max in raw score units (q.k)
+    float l_part = 0.f;
+    const float c2 = a.scale * kLog2e;
+    const float lam_raw = a.lambda / a.scale;
+    int n_exec = 0, n_skip = 0;
+    bool bad_col = false;
+
+    if (nt > 0) {
+        const int kb = tile_key0(0);
+        load_tile(kb);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        const int kb0 = tile_key0(t);
+        if (t + 1 < nt) load_tile(tile_key0(t + 1));  // in flight during this tile
+        if (kb0 < 0) bad_col = true;
+        if (kb0 >= 0 && wave_rows) {
+            const uint16_t* K = Ks[buf];
+            floatx16 s0, s1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(K + l32 * KSTR + ks * 16 + half * 8);
+                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(K + (32 + l32) * KSTR + ks * 16 + half * 8);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+            }
+            // masks only where a key can be past the sequence end or after a query of this wave
+            const bool need_mask = (kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0);
+            if (need_mask) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kk = kb0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool ok0 = kk < N && (!a.causal || kk <= qrow);
+                    const bool ok1 = kk + 32 < N && (!a.causal || kk + 32 <= qrow);
+                    s0[i] = ok0 ? s0[i] : -INFINITY;
+                    s1[i] = ok1 ? s1[i] : -INFINITY;
+                }
+            }
+            float smax = fmaxf(s0[0], s1[0]);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) smax = fmaxf(smax, fmaxf(s0[i], s1[i]));
+            smax = fmaxf(smax, __shfl_xor(smax, 32));
+            const float m_new = fmaxf(m_run, smax);
+            bool skip = false;
+            if constexpr (LAM) {
+                float gap = (row_valid && smax > -INFINITY) ? smax - m_new : -INFINITY;
+                gap = wave_max(gap);
+                skip = gap < lam_raw;
+            }
+            const float msafe = m_new == -INFINITY ? 0.f : m_new;
+            const float mc = msafe * c2;
+            const float alpha = __builtin_amdgcn_exp2f((m_run - msafe) * c2);
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
+                s0[i] = p0;
+                s1[i] = p1;
+                psum += p0 + p1;
+            }
+            l_part = fmaf(l_part, alpha, psum);
+            m_run = m_new;
+            if (LAM && a.pv_skip && lane == 0 && t % SUB == 0)
+                a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
+            if (skip) {
+                ++n_skip;
+            } else {
+                ++n_exec;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[tt][i] *= alpha;
+                }
+                bf16x8_t pb[4];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    pb[0][x] = (__bf16)s0[x];
+                    pb[1][x] = (__bf16)s0[8 + x];
+                    pb[2][x] = (__bf16)s1[x];
+                    pb[3][x] = (__bf16)s1[8 + x];
+                }
+                const uint16_t* V = Vt[buf];
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int ps = 0; ps < 4; ++ps) {
+                        const uint16_t* vp = V + (32 * tt + l32) * VSTR + ps * 16 + 4 * half;
+                        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+                        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+                        const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps], oacc[tt], 0, 0, 0);
+                    }
+            }
+        } else if (!wave_rows && LAM && a.pv_skip && lane == 0 && t % SUB == 0) {
+            a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
+        }
+        if (t + 1 < nt) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+    if (!LAM && a.pv_skip && lane == 0)
+        for (int e = e0; e < e1; ++e) a.pv_skip[int64_t(e) * 4 + wave] = 0;
+    if (bad_col && tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    if (row_valid) {
+        const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
+        if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
+        float* orow = Oh + int64_t(qrow) * D;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float4 v;
+                v.x = oacc[tt][4 * g + 0] * inv;
+                v.y = oacc[tt][4 * g + 1] * inv;
+                v.z = oacc[tt][4 * g + 2] * inv;
+                v.w = oacc[tt][4 * g + 3] * inv;
+                *reinterpret_cast<float4*>(orow + 32 * tt + 8 * g + 4 * half) = v;
+            }
+    }
+    if (a.counters) {
+        if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)(e1 > e0 ? e1 - e0 : 0));
+        if (lane == 0 && wave_rows) {
+            atomicAdd(&a.counters[1], (unsigned long long)((n_exec + SUB - 1) / SUB));
+            atomicAdd(&a.counters[2], (unsigned long long)(n_skip / SUB));
+        }
+    }
+}
+
 // 16x16 blocks: thread (r, c) owns query row r of the block and output
 // columns c, c+16, ...; scores go through LDS.  The whole 16-row block is one
 // PV-skip group.
@@ -367,17 +633,30 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int64_t rows = int64_t(a.B) * a.Hq * a.n_qb;
     if (rows > INT32_MAX) return hipErrorInvalidValue;
+    const bool lam_on = a.lambda > -INFINITY;
     const dim3 grid{unsigned(rows), 1, 1};
     const dim3 block{256, 1, 1};
     if (a.bq == 16 && a.bk == 16) {
         if (a.D == 128) hipLaunchKernelGGL(k_flash_small<128>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(k_flash_small<64>, grid, block, 0, stream, a);
-    } else if (a.bk == 64) {
-        if (a.D == 128) hipLaunchKernelGGL((k_flash_mfma<128, 64>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((k_flash_mfma<64, 64>), grid, block, 0, stream, a);
-    } else {
+    } else if (a.bk == 128 && lam_on) {
+        // a PV-skip decision needs all 128 keys of a block at once
         if (a.D == 128) hipLaunchKernelGGL((k_flash_mfma<128, 128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((k_flash_mfma<64, 128>), grid, block, 0, stream, a);
+    } else {
+        const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
+        if (a.bk == 64) {
+            if (lam_on) {
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 1, true>), pgrid, block, 0, stream, a);
+                else hipLaunchKernelGGL((k_flash_pipe<64, 1, true>), pgrid, block, 0, stream, a);
+            } else {
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 1, false>), pgrid, block, 0, stream, a);
+                else hipLaunchKernelGGL((k_flash_pipe<64, 1, false>), pgrid, block, 0, stream, a);
+            }
+        } else {
+            if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 2, false>), pgrid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_flash_pipe<64, 2, false>), pgrid, block, 0, stream, a);
+        }
     }
     return hipGetLastError();
 }
