@@ -1,0 +1,121 @@
+"""GPU parity at the workloads' full sizes (MI355X only), on sampled outputs.
+
+The whole path runs exactly as the benchmark runs it.  The oracle then checks
+what it can afford one by one: the full permutation and sampled permuted
+rows (bit-exact), the block statistics and predicted mask rows of sampled
+heads (exact except borderline rows), the full CSR against the GPU's own
+mask (bit-exact), the counters against the CSR and skip flags, and the
+outputs of sampled query blocks against fp64 on the GPU's CSR.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import image_dit_amd as sa  # noqa: E402
+from oracle import layout as OL  # noqa: E402
+from oracle import predict as OP  # noqa: E402
+from workloads import CONFIGS, generate  # noqa: E402
+
+import _ref as R  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+FULL = ["image", "video", "long_video", "causal_long"]
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    w = CONFIGS[name]
+    log(f"[full] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k}")
+    q, k, v = generate(w)
+    cfg = sa.config_from_workload(w)
+    path = sa.SparseAttentionPath(cfg)
+    mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    path.permute(qd, kd, vd)
+    path.predict(mask_out=mask)
+    path.attend()
+    path.unpermute()
+    torch.cuda.synchronize()
+    assert path.statuses() == (sa.SA_OK, sa.SA_OK)
+    del qd, kd, vd
+
+    rng = np.random.default_rng(12345)
+    perm = R.oracle_perm(w)
+    assert np.array_equal(path.perm_host.astype(np.int64), perm)
+    # sampled permuted rows, bit-exact
+    for src, dst, H in ((q, path.qp, w.Hq), (k, path.kp, w.Hkv), (v, path.vp, w.Hkv)):
+        bs, hs, ts = rng.integers(0, w.B, 64), rng.integers(0, H, 64), rng.integers(0, w.N, 64)
+        got = dst[torch.from_numpy(bs).cuda(), torch.from_numpy(hs).cuda(), torch.from_numpy(ts).cuda()]
+        got = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, src[bs, hs, perm[ts]])
+
+    gmask = mask.cpu().numpy().astype(bool)
+    rp, ci = path.csr_host()
+    rp_m, ci_m = OP.mask_to_csr(gmask)
+    assert np.array_equal(rp, rp_m) and np.array_equal(ci, ci_m)
+    skip = path.pv_skip.cpu().numpy()[:int(rp[-1]) * path.groups]
+    cnt = path.counters.cpu().numpy()
+    assert cnt[0] == int(rp[-1])
+    i_of_row = np.arange(cfg.rows) % cfg.n_qb
+    qrows = np.minimum((i_of_row + 1) * w.block_q, w.N) - i_of_row * w.block_q
+    ngr = -(-qrows // 32)
+    real = int(np.sum(ngr * np.diff(rp)))
+    assert cnt[1] + cnt[2] == real
+    ent_row = np.repeat(np.arange(cfg.rows), np.diff(rp))
+    flags = skip.reshape(-1, path.groups)
+    live = np.arange(path.groups)[None, :] < ngr[ent_row][:, None]
+    assert cnt[2] == int(flags[live].sum())
+
+    mp = R.mask_params(w)
+    G = w.Hq // w.Hkv
+    o = path.o.cpu().numpy() if w.B * w.Hq * w.N * w.D < 2e8 else None
+    heads = [(0, 0), (w.B - 1, w.Hq - 1)]
+    n_bad = n_border = n_rows = 0
+    worst_max, sum_abs, n_el = 0.0, 0.0, 0
+    for b, h in heads:
+        hk = h // G
+        qp = R.permuted(q[b, h], perm)
+        kp = R.permuted(k[b, hk], perm)
+        vp = R.permuted(v[b, hk], perm)
+        rows = sorted(set(np.linspace(0, cfg.n_qb - 1, 24).astype(int).tolist()))
+        ref = OP.predict_head(qp, kp, mp, rows=rows)
+        r0 = (b * w.Hq + h) * cfg.n_qb
+        gm = gmask[r0:r0 + cfg.n_qb]
+        bad, border, checked = R.compare_head_mask(gm, ref, rows)
+        n_bad += len(bad)
+        n_border += len(border)
+        n_rows += checked
+        qbar = path.workspace_view(0, torch.float32, (cfg.B, cfg.Hq, cfg.n_qb, cfg.D))[b, h].cpu().numpy()
+        assert np.allclose(qbar, ref["qbar"], rtol=1e-5, atol=1e-5)
+        qblocks = rows[:: max(1, len(rows) // 6)]
+        ys, recs = R.attend_rows(qp, kp, vp, w, rp, ci, r0, qblocks, skip, path.groups)
+        for i, y in ys.items():
+            toks = perm[i * w.block_q:i * w.block_q + y.shape[0]]
+            got = o[b, h, toks] if o is not None else \
+                path.o[b, h, torch.from_numpy(toks).cuda()].cpu().numpy()
+            d = np.abs(got - y)
+            worst_max = max(worst_max, float(d.max()))
+            sum_abs += float(d.sum())
+            n_el += d.size
+            if w.lam is not None:
+                far, _ = R.lambda_disagreements(recs[i], w.lam)
+                assert far == 0
+    log(f"[full] {name}: nnz={int(rp[-1])} sampled_rows={n_rows} mismatch={n_bad} borderline={n_border} "
+        f"out_max={worst_max:.3e} out_mean={sum_abs / n_el:.3e} pv_exec={cnt[1]} pv_skip={cnt[2]}")
+    assert n_bad == 0
+    assert worst_max <= R.MAX_ABS and sum_abs / n_el <= R.MEAN_ABS
