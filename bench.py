@@ -288,7 +288,7 @@ def main():
         "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_flash_mfma (+ k_attn_init), per sa_sparse_attn_fwd call",
+            "kernel": "k_flash_dma (+ k_attn_init), per sa_sparse_attn_fwd call",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

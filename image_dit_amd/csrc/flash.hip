@@ -3,6 +3,9 @@
 // blocks outside the mask skip both QK^T and PV; section 2.3: PV skip when
 // the running-max gap of a row group is below lambda).
 //
+// k_flash_dma<D, SUB, LAM>: the production kernel for 64-key tiles (and for
+// 128-key blocks without PV skip, as two 64-key steps); see its comment.
+//
 // k_flash_mfma<D, BK>: one workgroup of 4 wavefronts per 128-row query block;
 // wavefront w owns query rows 32w..32w+31 and is the PV-skip group.  Scores
 // are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that
@@ -34,6 +37,24 @@ __device__ inline float wave_max(float v) {
 }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over one head's rows: loads at or past `bytes` return 0
+// (hardware range check), which covers the ragged last block and any
+// out-of-range column without branches.
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
 
 __global__ void k_attn_init(int32_t* status, unsigned long long* counters) {
     *status = SA_OK;
@@ -245,31 +266,60 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     }
 }
 
-// Pipelined variant for 64-key tiles.  Each CSR entry covers SUB consecutive
-// 64-key tiles (SUB = 2 runs 128-key blocks as two online-softmax steps,
-// which is exact when no PV-skip decision needs the whole 128 keys).
-// K and V^T tiles are double-buffered in LDS: the global loads of tile t+1
-// are issued into registers before tile t is computed and written to the
-// other LDS buffer afterwards, so one barrier per tile suffices and the load
-// latency hides behind the MFMA/softmax work of this and the co-resident
-// workgroup.  Workgroups are mapped so that each XCD (workgroup id mod 8)
-// walks a contiguous range of (head, query block) rows: the K/V of the few
-// heads an XCD works on stay in its L2 and in the shared last-level cache.
+// Small helpers of the pipelined kernels.
+__device__ inline float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// (value of this lane, value of lane ^ 32) combined: returns both halves' values
+__device__ inline void swap32(float v, float& lo, float& hi) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    lo = __uint_as_float(pr[0]);
+    hi = __uint_as_float(pr[1]);
+}
+// max over lanes 0..31 (lanes 32..63 hold the same values), uniform result
+__device__ inline float max_lanes32(float v) {
+    v = fmaxf(v, __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), 0x140, 0xF, 0xF, false)));
+    const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+    const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+    return fmaxf(r0, r1);
+}
+
+// DMA variant (the production path for 64-key tiles).  K and V tiles go
+// straight from HBM/L2 into LDS with buffer_load ... lds (16 bytes per lane,
+// rows past the sequence end read as zero), double-buffered: the DMA of tile
+// t+1 runs while tile t is computed, one vmcnt wait + barrier per tile.  Both
+// tiles stay row-major in LDS with an XOR swizzle of the 16-byte chunks, so
+// the K operand reads (ds_read_b128) and the transposed V operand reads
+// (ds_read_b64_tr_b16: in each 16-lane group, lane i slot j receives element
+// i&3 of the 8 bytes read by lane 4j + i/4) are bank-conflict free.  No
+// staging registers, no register transpose of V.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ inline int chunk_swz(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return (r >> 1) & 7;
+}
+
 template <int D, int SUB, bool LAM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_flash_pipe(FlashArgs a) {
+void k_flash_dma(FlashArgs a) {
     constexpr int BQ = 128;
     constexpr int BK = 64;
-    constexpr int KSTR = D + 8;
-    constexpr int VSTR = BK + 4;
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;            // rows per 1 KB DMA instruction
+    constexpr int IPW = BK / RPI / 4;        // DMA instructions per wave per tile
     constexpr int NT = D / 32;
     constexpr int KS = D / 16;
-    constexpr int KCH = D / 8;                      // 16-byte chunks per K row
-    constexpr int KL = BK * KCH / 256;              // K chunks per thread
-    constexpr int DB4 = D / 4;
-    constexpr int VL = (BK / 4) * DB4 / 256;        // 4x4 V blocks per thread
-    __shared__ __align__(16) uint16_t Ks[2][BK * KSTR];
-    __shared__ __align__(16) uint16_t Vt[2][D * VSTR];
+    __shared__ __align__(16) uint16_t Ks[2][BK * D];
+    __shared__ __align__(16) uint16_t Vs[2][BK * D];
 
     const int G = a.B * a.Hq * a.n_qb;
     const int per = (G + 7) >> 3;
@@ -281,13 +331,12 @@ void k_flash_pipe(FlashArgs a) {
     const int b = bh / a.Hq;
     const int hk = hq / (a.Hq / a.Hkv);
     const int N = int(a.N);
-    const uint16_t* Qh = a.q + int64_t(bh) * N * D;
-    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * N * D;
-    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * N * D;
-    float* Oh = a.o + int64_t(bh) * N * D;
+    const uint32_t head_bytes = uint32_t(N) * D * 2u;
+    const __amdgpu_buffer_rsrc_t rK = head_rsrc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t rV = head_rsrc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
@@ -297,29 +346,12 @@ void k_flash_pipe(FlashArgs a) {
     const bool wave_rows = wrow0 < N;
 
     bf16x8_t qf[KS];
+    {
+        const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4*>(Qh + int64_t(qrow) * D + ks * 16 + half * 8);
-        qf[ks] = as_bf16x8(u);
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qrow * D + ks * 16 + half * 8) * 2u));
     }
-
-    // per-thread staging geometry (fixed for the whole kernel)
-    int k_r[KL], k_c[KL], v_k[VL], v_d[VL];
-#pragma unroll
-    for (int c = 0; c < KL; ++c) {
-        const int idx = tid + 256 * c;
-        k_r[c] = idx / KCH;
-        k_c[c] = idx % KCH;
-    }
-#pragma unroll
-    for (int c = 0; c < VL; ++c) {
-        const int idx = tid + 256 * c;
-        v_k[c] = idx / DB4;
-        v_d[c] = idx % DB4;
-    }
-    uint4 kreg[KL];
-    uint2 vreg[VL][4];
 
     const int e0 = a.row_ptr[row];
     int e1 = a.row_ptr[row + 1];
@@ -327,48 +359,27 @@ void k_flash_pipe(FlashArgs a) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
     }
-    const int nt = (e1 > e0 ? e1 - e0 : 0) * SUB;  // 64-key tiles to visit
+    const int nt = (e1 > e0 ? e1 - e0 : 0) * SUB;
 
-    // tile index t -> first key (or -1 for an out-of-range column)
     auto tile_key0 = [&](int t) -> int {
         const int j = a.col_idx[e0 + t / SUB];
         if (j < 0 || j >= a.n_kb) return -1;
         return j * (BK * SUB) + (t % SUB) * BK;
     };
-    auto load_tile = [&](int kb0) {
+    // this lane's part of each DMA instruction: local row and swizzled source chunk
+    const int dma_r = lane / CPR;
+    const int dma_p = lane % CPR;
+    auto issue_tile = [&](int kb0, int buf) {
 #pragma unroll
-        for (int c = 0; c < KL; ++c) {
-            const int key = kb0 + k_r[c];
-            kreg[c] = (kb0 >= 0 && key < N)
-                          ? *reinterpret_cast<const uint4*>(Kh + int64_t(key) * D + k_c[c] * 8)
-                          : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < IPW; ++c) {
+            const int r = (wave * IPW + c) * RPI + dma_r;
+            const uint32_t off = kb0 < 0 ? 0x80000000u
+                                         : uint32_t(kb0 + r) * (D * 2u) + uint32_t((dma_p ^ chunk_swz<D>(r)) * 16);
+            lds_void* kd = (lds_void*)(&Ks[buf][(wave * IPW + c) * 512]);
+            lds_void* vd = (lds_void*)(&Vs[buf][(wave * IPW + c) * 512]);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, kd, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, vd, 16, off, 0, 0, 0);
         }
-#pragma unroll
-        for (int c = 0; c < VL; ++c)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = kb0 + v_k[c] * 4 + rr;
-                vreg[c][rr] = (kb0 >= 0 && key < N)
-                                  ? *reinterpret_cast<const uint2*>(Vh + int64_t(key) * D + v_d[c] * 4)
-                                  : make_uint2(0, 0);
-            }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < KL; ++c)
-            *reinterpret_cast<uint4*>(&Ks[buf][k_r[c] * KSTR + k_c[c] * 8]) = kreg[c];
-#pragma unroll
-        for (int c = 0; c < VL; ++c)
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int sh = (cc & 1) * 16;
-                const uint32_t x0 = ((cc < 2 ? vreg[c][0].x : vreg[c][0].y) >> sh) & 0xffffu;
-                const uint32_t x1 = ((cc < 2 ? vreg[c][1].x : vreg[c][1].y) >> sh) & 0xffffu;
-                const uint32_t x2 = ((cc < 2 ? vreg[c][2].x : vreg[c][2].y) >> sh) & 0xffffu;
-                const uint32_t x3 = ((cc < 2 ? vreg[c][3].x : vreg[c][3].y) >> sh) & 0xffffu;
-                *reinterpret_cast<uint2*>(&Vt[buf][(v_d[c] * 4 + cc) * VSTR + v_k[c] * 4]) =
-                    make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-            }
     };
 
     floatx16 oacc[NT];
@@ -383,30 +394,36 @@ void k_flash_pipe(FlashArgs a) {
     int n_exec = 0, n_skip = 0;
     bool bad_col = false;
 
-    if (nt > 0) {
-        const int kb = tile_key0(0);
-        load_tile(kb);
-        store_tile(0);
-    }
+    // transposed-V read geometry for this lane (see the comment above)
+    const int tr_j = (lane & 15) >> 2;
+    const int tr_m = lane & 3;
+    const int tr_g = (lane >> 4) & 1;
+
+    if (nt > 0) issue_tile(tile_key0(0), 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
         const int buf = t & 1;
         const int kb0 = tile_key0(t);
-        if (t + 1 < nt) load_tile(tile_key0(t + 1));  // in flight during this tile
-        if (kb0 < 0) bad_col = true;
-        if (kb0 >= 0 && wave_rows) {
+        if (t + 1 < nt) issue_tile(tile_key0(t + 1), buf ^ 1);
+        if (kb0 < 0) {
+            bad_col = true;
+        } else if (!wave_rows) {
+            if (LAM && a.pv_skip && lane == 0 && t % SUB == 0) a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
+        } else {
             const uint16_t* K = Ks[buf];
             floatx16 s0, s1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(K + l32 * KSTR + ks * 16 + half * 8);
-                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(K + (32 + l32) * KSTR + ks * 16 + half * 8);
+                const int c = ks * 2 + half;
+                const int r0 = l32, r1 = 32 + l32;
+                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(K + r0 * D + ((c ^ chunk_swz<D>(r0)) * 8));
+                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(K + r1 * D + ((c ^ chunk_swz<D>(r1)) * 8));
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
-            // masks only where a key can be past the sequence end or after a query of this wave
             const bool need_mask = (kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0);
             if (need_mask) {
 #pragma unroll
@@ -418,30 +435,36 @@ void k_flash_pipe(FlashArgs a) {
                     s1[i] = ok1 ? s1[i] : -INFINITY;
                 }
             }
-            float smax = fmaxf(s0[0], s1[0]);
+            float mx[4];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) smax = fmaxf(smax, fmaxf(s0[i], s1[i]));
-            smax = fmaxf(smax, __shfl_xor(smax, 32));
+            for (int r = 0; r < 4; ++r) {
+                const float m1 = max3f(s0[4 * r], s0[4 * r + 1], s0[4 * r + 2]);
+                const float m2 = max3f(s0[4 * r + 3], s1[4 * r], s1[4 * r + 1]);
+                mx[r] = max3f(m1, m2, fmaxf(s1[4 * r + 2], s1[4 * r + 3]));
+            }
+            float lo, hi;
+            swap32(max3f(mx[0], mx[1], fmaxf(mx[2], mx[3])), lo, hi);
+            const float smax = fmaxf(lo, hi);
             const float m_new = fmaxf(m_run, smax);
             bool skip = false;
             if constexpr (LAM) {
-                float gap = (row_valid && smax > -INFINITY) ? smax - m_new : -INFINITY;
-                gap = wave_max(gap);
-                skip = gap < lam_raw;
+                const float gap = (row_valid && smax > -INFINITY) ? smax - m_new : -INFINITY;
+                skip = max_lanes32(gap) < lam_raw;
             }
             const float msafe = m_new == -INFINITY ? 0.f : m_new;
             const float mc = msafe * c2;
             const float alpha = __builtin_amdgcn_exp2f((m_run - msafe) * c2);
-            float psum = 0.f;
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
                 s0[i] = p0;
                 s1[i] = p1;
-                psum += p0 + p1;
+                ps0 += p0;
+                ps1 += p1;
             }
-            l_part = fmaf(l_part, alpha, psum);
+            l_part = fmaf(l_part, alpha, ps0 + ps1);
             m_run = m_new;
             if (LAM && a.pv_skip && lane == 0 && t % SUB == 0)
                 a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
@@ -463,33 +486,38 @@ void k_flash_pipe(FlashArgs a) {
                     pb[2][x] = (__bf16)s1[x];
                     pb[3][x] = (__bf16)s1[8 + x];
                 }
-                const uint16_t* V = Vt[buf];
+                const uint16_t* V = Vs[buf];
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int dv = 32 * tt + 16 * tr_g + 4 * tr_m;
 #pragma unroll
                     for (int ps = 0; ps < 4; ++ps) {
-                        const uint16_t* vp = V + (32 * tt + l32) * VSTR + ps * 16 + 4 * half;
-                        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-                        const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                        const int key_a = 16 * ps + 4 * half + tr_j;
+                        const int key_b = key_a + 8;
+                        const uint16_t* pa = V + key_a * D + (((dv >> 3) ^ chunk_swz<D>(key_a)) * 8) + (dv & 7);
+                        const uint16_t* pbp = V + key_b * D + (((dv >> 3) ^ chunk_swz<D>(key_b)) * 8) + (dv & 7);
+                        const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
+                        const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pbp);
+                        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
                         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps], oacc[tt], 0, 0, 0);
                     }
+                }
             }
-        } else if (!wave_rows && LAM && a.pv_skip && lane == 0 && t % SUB == 0) {
-            a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
         }
-        if (t + 1 < nt) store_tile(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for tile t+1 has landed
+        __syncthreads();                // ... and everyone's; buffer `buf` is free again
     }
     if (!LAM && a.pv_skip && lane == 0)
         for (int e = e0; e < e1; ++e) a.pv_skip[int64_t(e) * 4 + wave] = 0;
     if (bad_col && tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
 
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    float l_lo, l_hi;
+    swap32(l_part, l_lo, l_hi);
+    const float l_tot = l_lo + l_hi;
     if (row_valid) {
         const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
         if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
-        float* orow = Oh + int64_t(qrow) * D;
+        float* orow = a.o + int64_t(bh) * N * D + int64_t(qrow) * D;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -647,15 +675,15 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
         const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
         if (a.bk == 64) {
             if (lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 1, true>), pgrid, block, 0, stream, a);
-                else hipLaunchKernelGGL((k_flash_pipe<64, 1, true>), pgrid, block, 0, stream, a);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, true>), pgrid, block, 0, stream, a);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, true>), pgrid, block, 0, stream, a);
             } else {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 1, false>), pgrid, block, 0, stream, a);
-                else hipLaunchKernelGGL((k_flash_pipe<64, 1, false>), pgrid, block, 0, stream, a);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, false>), pgrid, block, 0, stream, a);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, false>), pgrid, block, 0, stream, a);
             }
         } else {
-            if (a.D == 128) hipLaunchKernelGGL((k_flash_pipe<128, 2, false>), pgrid, block, 0, stream, a);
-            else hipLaunchKernelGGL((k_flash_pipe<64, 2, false>), pgrid, block, 0, stream, a);
+            if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, false>), pgrid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_flash_dma<64, 2, false>), pgrid, block, 0, stream, a);
         }
     }
     return hipGetLastError();
