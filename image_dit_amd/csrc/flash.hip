@@ -310,7 +310,8 @@ __device__ inline int chunk_swz(int r) {
 
 template <int D, int SUB, bool LAM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_flash_dma(FlashArgs a) {
+void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                 uint8_t* __restrict__ pv_skip) {
     constexpr int BQ = 128;
     constexpr int BK = 64;
     constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -353,8 +354,8 @@ void k_flash_dma(FlashArgs a) {
             qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qrow * D + ks * 16 + half * 8) * 2u));
     }
 
-    const int e0 = a.row_ptr[row];
-    int e1 = a.row_ptr[row + 1];
+    const int e0 = row_ptr[row];
+    int e1 = row_ptr[row + 1];
     if (e1 > a.col_cap) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
@@ -362,25 +363,35 @@ void k_flash_dma(FlashArgs a) {
     const int nt = (e1 > e0 ? e1 - e0 : 0) * SUB;
 
     auto tile_key0 = [&](int t) -> int {
-        const int j = a.col_idx[e0 + t / SUB];
+        const int j = col_idx[e0 + t / SUB];
         if (j < 0 || j >= a.n_kb) return -1;
         return j * (BK * SUB) + (t % SUB) * BK;
     };
     // this lane's part of each DMA instruction: local row and swizzled source chunk
     const int dma_r = lane / CPR;
     const int dma_p = lane % CPR;
-    auto issue_tile = [&](int kb0, int buf) {
-#pragma unroll
-        for (int c = 0; c < IPW; ++c) {
-            const int r = (wave * IPW + c) * RPI + dma_r;
-            const uint32_t off = kb0 < 0 ? 0x80000000u
-                                         : uint32_t(kb0 + r) * (D * 2u) + uint32_t((dma_p ^ chunk_swz<D>(r)) * 16);
-            lds_void* kd = (lds_void*)(&Ks[buf][(wave * IPW + c) * 512]);
-            lds_void* vd = (lds_void*)(&Vs[buf][(wave * IPW + c) * 512]);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, kd, 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, vd, 16, off, 0, 0, 0);
-        }
+    // DMA instruction slot `slot` (0 .. 4*IPW-1) of a 64-key tile of `src` into `dst`
+    auto dma = [&](__amdgpu_buffer_rsrc_t src, uint16_t* dst, int kb0, int slot) {
+        const int r = slot * RPI + dma_r;
+        const uint32_t off = kb0 < 0 ? 0x80000000u
+                                     : uint32_t(kb0 + r) * (D * 2u) + uint32_t((dma_p ^ chunk_swz<D>(r)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(dst + slot * 512), 16, off, 0, 0, 0);
     };
+    auto issue_k = [&](int kb0, int buf) {
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) dma(rK, Ks[buf], kb0, wave * IPW + c);
+    };
+    auto issue_v = [&](int kb0, int buf) {  // this wave's share of the V tile
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) dma(rV, Vs[buf], kb0, wave * IPW + c);
+    };
+    auto issue_v_all = [&](int kb0, int buf) {  // the whole V tile by this wave alone
+#pragma unroll 1
+        for (int c = 0; c < 4 * IPW; ++c) dma(rV, Vs[buf], kb0, c);
+    };
+    // PV-skip bookkeeping: need[t & 1][w] = wave w ran the PV product of tile t
+    __shared__ int need[2][4];
+    int v_ready = 3;  // bit b: the V tile of LDS buffer b was fetched
 
     floatx16 oacc[NT];
 #pragma unroll
@@ -399,17 +410,31 @@ void k_flash_dma(FlashArgs a) {
     const int tr_m = lane & 3;
     const int tr_g = (lane >> 4) & 1;
 
-    if (nt > 0) issue_tile(tile_key0(0), 0);
+    if (nt > 0) {
+        issue_k(tile_key0(0), 0);
+        issue_v(tile_key0(0), 0);
+    }
+    if (lane == 0) need[1][wave] = 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
         const int buf = t & 1;
         const int kb0 = tile_key0(t);
-        if (t + 1 < nt) issue_tile(tile_key0(t + 1), buf ^ 1);
+        if (t + 1 < nt) {
+            const int kn = tile_key0(t + 1);
+            issue_k(kn, buf ^ 1);
+            // with PV skip on, V of the next tile is fetched only if some wave
+            // ran the PV product of the previous tile (runs of skips are long)
+            bool want_v = true;
+            if constexpr (LAM) want_v = (need[buf ^ 1][0] | need[buf ^ 1][1] | need[buf ^ 1][2] | need[buf ^ 1][3]) != 0;
+            if (want_v) issue_v(kn, buf ^ 1);
+            v_ready = want_v ? (v_ready | (2 >> buf)) : (v_ready & ~(2 >> buf));
+        }
+        int my_need = 0;
         if (kb0 < 0) {
             bad_col = true;
         } else if (!wave_rows) {
-            if (LAM && a.pv_skip && lane == 0 && t % SUB == 0) a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
+            if (LAM && pv_skip && lane == 0 && t % SUB == 0) pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
         } else {
             const uint16_t* K = Ks[buf];
             floatx16 s0, s1;
@@ -466,12 +491,19 @@ void k_flash_dma(FlashArgs a) {
             }
             l_part = fmaf(l_part, alpha, ps0 + ps1);
             m_run = m_new;
-            if (LAM && a.pv_skip && lane == 0 && t % SUB == 0)
-                a.pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
+            if (LAM && pv_skip && lane == 0 && t % SUB == 0)
+                pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
             if (skip) {
                 ++n_skip;
             } else {
                 ++n_exec;
+                my_need = 1;
+                if (LAM && !((v_ready >> buf) & 1)) {
+                    // not prefetched: fetch the whole tile now (other waves may do the
+                    // same concurrently; they write identical bytes)
+                    issue_v_all(kb0, buf);
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
                 if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt)
@@ -504,11 +536,12 @@ void k_flash_dma(FlashArgs a) {
                 }
             }
         }
+        if (lane == 0) need[buf][wave] = my_need;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for tile t+1 has landed
         __syncthreads();                // ... and everyone's; buffer `buf` is free again
     }
-    if (!LAM && a.pv_skip && lane == 0)
-        for (int e = e0; e < e1; ++e) a.pv_skip[int64_t(e) * 4 + wave] = 0;
+    if (!LAM && pv_skip && lane == 0)
+        for (int e = e0; e < e1; ++e) pv_skip[int64_t(e) * 4 + wave] = 0;
     if (bad_col && tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
 
     float l_lo, l_hi;
@@ -675,15 +708,15 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
         const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
         if (a.bk == 64) {
             if (lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, true>), pgrid, block, 0, stream, a);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, true>), pgrid, block, 0, stream, a);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             } else {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, false>), pgrid, block, 0, stream, a);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, false>), pgrid, block, 0, stream, a);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             }
         } else {
-            if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, false>), pgrid, block, 0, stream, a);
-            else hipLaunchKernelGGL((k_flash_dma<64, 2, false>), pgrid, block, 0, stream, a);
+            if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+            else hipLaunchKernelGGL((k_flash_dma<64, 2, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
         }
     }
     return hipGetLastError();
