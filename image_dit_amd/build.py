@@ -43,6 +43,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel template whose host-side instantiation failed leaves its launch
+    # stub undefined without any diagnostic: refuse such a library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "device_stub" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

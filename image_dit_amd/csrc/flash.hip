@@ -292,20 +292,22 @@ __device__ inline float max_lanes32(float v) {
 // DMA variant (the production path for 64-key tiles).  K and V tiles go
 // straight from HBM/L2 into LDS with buffer_load ... lds (16 bytes per lane,
 // rows past the sequence end read as zero), double-buffered: the DMA of tile
-// t+1 runs while tile t is computed, one vmcnt wait + barrier per tile.  Both
-// tiles stay row-major in LDS with an XOR swizzle of the 16-byte chunks, so
-// the K operand reads (ds_read_b128) and the transposed V operand reads
-// (ds_read_b64_tr_b16: in each 16-lane group, lane i slot j receives element
-// i&3 of the 8 bytes read by lane 4j + i/4) are bank-conflict free.  No
-// staging registers, no register transpose of V.
+// t+1 runs while tile t is computed, one vmcnt wait + barrier per tile.
+// Each 1 KB DMA instruction moves 8 rows x 128 bytes (whole cache lines); in
+// LDS the 16-byte chunks of row r are XOR-permuted (K: by (r>>1)&7, V: by
+// r&7) so that the MFMA operand reads are bank-conflict free: the K operand
+// (ds_read_b128, key row 32mt+(l&31), head-dim chunk 2ks+(l>>5)) and the
+// transposed V operand (ds_read_b64_tr_b16: in each 16-lane group lane i slot
+// j receives element i&3 of the 8 bytes lane 4j+i/4 read, so lane l reads
+// V[16ps + 8ab + 4(l>>5) + ((l&15)>>2)][32tt + 16((l>>4)&1) + 4(l&3) .. +3]).
+// All read addresses are one of a few per-lane offsets plus an immediate.
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D>
-__device__ inline int chunk_swz(int r) {
-    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return (r >> 1) & 7;
+// 16 bytes per lane from buffer `r` at byte offset `off` into LDS at dst + 16*lane
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
 template <int D, int SUB, bool LAM>
@@ -314,11 +316,10 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                  uint8_t* __restrict__ pv_skip) {
     constexpr int BQ = 128;
     constexpr int BK = 64;
-    constexpr int CPR = D / 8;               // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;            // rows per 1 KB DMA instruction
-    constexpr int IPW = BK / RPI / 4;        // DMA instructions per wave per tile
-    constexpr int NT = D / 32;
-    constexpr int KS = D / 16;
+    constexpr int NT = D / 32;               // 32-wide output column tiles
+    constexpr int KS = D / 16;               // MFMA k-steps over the head dim
+    constexpr int SEG = D / 64;              // 128-byte segments per row
+    constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
     __shared__ __align__(16) uint16_t Ks[2][BK * D];
     __shared__ __align__(16) uint16_t Vs[2][BK * D];
 
@@ -367,28 +368,46 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         if (j < 0 || j >= a.n_kb) return -1;
         return j * (BK * SUB) + (t % SUB) * BK;
     };
-    // this lane's part of each DMA instruction: local row and swizzled source chunk
-    const int dma_r = lane / CPR;
-    const int dma_p = lane % CPR;
-    // DMA instruction slot `slot` (0 .. 4*IPW-1) of a 64-key tile of `src` into `dst`
-    auto dma = [&](__amdgpu_buffer_rsrc_t src, uint16_t* dst, int kb0, int slot) {
-        const int r = slot * RPI + dma_r;
-        const uint32_t off = kb0 < 0 ? 0x80000000u
-                                     : uint32_t(kb0 + r) * (D * 2u) + uint32_t((dma_p ^ chunk_swz<D>(r)) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(dst + slot * 512), 16, off, 0, 0, 0);
+    // DMA: instruction idx covers rows 8*rg .. 8*rg+7 (rg = idx / SEG) of segment idx % SEG;
+    // lane L moves row 8*rg + L/8, LDS position L%8, i.e. source chunk (L%8) ^ swizzle(row)
+    const int dq = lane >> 3, dp = lane & 7;
+    const uint32_t k_lane[2] = {uint32_t(dq * D * 2 + ((dp ^ ((dq >> 1) & 7)) * 16)),
+                                uint32_t(dq * D * 2 + ((dp ^ ((4 + (dq >> 1)) & 7)) * 16))};
+    const uint32_t v_lane = uint32_t(dq * D * 2 + ((dp ^ dq) * 16));
+    auto tile_base = [&](int kb0, int idx) -> uint32_t {  // uniform part of the source offset
+        const int rg = idx / SEG, seg = idx % SEG;
+        return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
     };
     auto issue_k = [&](int kb0, int buf) {
 #pragma unroll
-        for (int c = 0; c < IPW; ++c) dma(rK, Ks[buf], kb0, wave * IPW + c);
+        for (int c = 0; c < DI; ++c) {
+            const int idx = wave * DI + c;
+            dma16(rK, &Ks[buf][idx * 512], k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+        }
     };
     auto issue_v = [&](int kb0, int buf) {  // this wave's share of the V tile
 #pragma unroll
-        for (int c = 0; c < IPW; ++c) dma(rV, Vs[buf], kb0, wave * IPW + c);
+        for (int c = 0; c < DI; ++c) {
+            const int idx = wave * DI + c;
+            dma16(rV, &Vs[buf][idx * 512], v_lane + tile_base(kb0, idx));
+        }
     };
     auto issue_v_all = [&](int kb0, int buf) {  // the whole V tile by this wave alone
 #pragma unroll 1
-        for (int c = 0; c < 4 * IPW; ++c) dma(rV, Vs[buf], kb0, c);
+        for (int idx = 0; idx < 4 * DI; ++idx)
+            dma16(rV, &Vs[buf][idx * 512], v_lane + tile_base(kb0, idx));
     };
+    // operand read offsets (elements): K for ks % 4, V for tt % 2
+    int k_off[4], v_off[2];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+        k_off[k4] = ((l32 >> 3) * SEG * 1024 + (l32 & 7) * 128 + (((2 * k4 + half) ^ ((l32 >> 1) & 7)) * 16)) / 2;
+    {
+        const int g = (lane >> 4) & 1, j = (lane & 15) >> 2, m = lane & 3;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            v_off[x] = ((4 * half + j) * 128 + (((4 * x + 2 * g + (m >> 1)) ^ (4 * half + j)) * 16) + 8 * (m & 1)) / 2;
+    }
     // PV-skip bookkeeping: need[t & 1][w] = wave w ran the PV product of tile t
     __shared__ int need[2][4];
     int v_ready = 3;  // bit b: the V tile of LDS buffer b was fetched
@@ -404,11 +423,6 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const float lam_raw = a.lambda / a.scale;
     int n_exec = 0, n_skip = 0;
     bool bad_col = false;
-
-    // transposed-V read geometry for this lane (see the comment above)
-    const int tr_j = (lane & 15) >> 2;
-    const int tr_m = lane & 3;
-    const int tr_g = (lane >> 4) & 1;
 
     if (nt > 0) {
         issue_k(tile_key0(0), 0);
@@ -442,10 +456,9 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int c = ks * 2 + half;
-                const int r0 = l32, r1 = 32 + l32;
-                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(K + r0 * D + ((c ^ chunk_swz<D>(r0)) * 8));
-                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(K + r1 * D + ((c ^ chunk_swz<D>(r1)) * 8));
+                const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
+                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
+                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
@@ -518,18 +531,13 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                     pb[2][x] = (__bf16)s1[x];
                     pb[3][x] = (__bf16)s1[8 + x];
                 }
-                const uint16_t* V = Vs[buf];
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
-                    const int dv = 32 * tt + 16 * tr_g + 4 * tr_m;
 #pragma unroll
                     for (int ps = 0; ps < 4; ++ps) {
-                        const int key_a = 16 * ps + 4 * half + tr_j;
-                        const int key_b = key_a + 8;
-                        const uint16_t* pa = V + key_a * D + (((dv >> 3) ^ chunk_swz<D>(key_a)) * 8) + (dv & 7);
-                        const uint16_t* pbp = V + key_b * D + (((dv >> 3) ^ chunk_swz<D>(key_b)) * 8) + (dv & 7);
+                        const uint16_t* pa = Vs[buf] + v_off[tt & 1] + ((2 * ps) * SEG + (tt >> 1)) * 512;
                         const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
-                        const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pbp);
+                        const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(pa + SEG * 512));
                         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
                         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps], oacc[tt], 0, 0, 0);
                     }
