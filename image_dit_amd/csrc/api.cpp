@@ -61,7 +61,7 @@ int predict_shape(const sa_mask_params* p, PredictShape* s) {
     s->off[2] = o; o = align_up(o + qblk * 4);
     s->off[3] = o; o = align_up(o + kblk * 4);
     s->off[4] = o; o = align_up(o + qblk * s->n_kb);
-    s->off[5] = o; o = align_up(o + qblk * 4);
+    s->off[5] = o; o = align_up(o + (qblk + topcdf_groups(int64_t(p->B) * p->Hq, s->n_qb)) * 4);
     s->bytes = size_t(o);
     return SA_OK;
 }
@@ -160,7 +160,7 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
 
     TopCdfArgs a;
     a.qbar = qbar; a.kbar = kbar; a.simq = simq; a.simk = simk;
-    a.mask = mask; a.counts = counts;
+    a.mask = mask; a.counts = counts; a.group_tot = counts + s.rows;
     a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.N = s.N;
     a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb);
     a.causal = p->causal; a.window = p->window;
@@ -173,7 +173,8 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
     e = launch_topcdf(a, hs);
     if (e != hipSuccess) return SA_ERR_HIP;
 
-    e = launch_csr(mask, counts, s.rows, int(s.n_kb), row_ptr, col_idx, col_cap, dev_status, hs);
+    e = launch_csr(mask, counts, a.group_tot, int64_t(s.B) * s.Hq, int(s.n_qb), int(s.n_kb), row_ptr, col_idx,
+                   col_cap, dev_status, hs);
     if (e != hipSuccess) return SA_ERR_HIP;
 
     if (mask_out) {

@@ -39,6 +39,7 @@ struct TopCdfArgs {
     const float* simk;
     uint8_t* mask;
     int32_t* counts;
+    int32_t* group_tot;  // kept blocks per group of 16 query blocks
     int B, Hq, Hkv, D;
     int64_t N;
     int bq, bk;
@@ -56,8 +57,10 @@ hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Predic
                               float* qbar, float* kbar, float* simq, float* simk,
                               int32_t* dev_status, hipStream_t stream);
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream);
-hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, int64_t rows, int n_kb,
-                      int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+// Number of TopCdf groups (16 consecutive query blocks of one head).
+int64_t topcdf_groups(int64_t bh, int64_t n_qb);
+hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t* group_tot, int64_t bh,
+                      int n_qb, int n_kb, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
                       int32_t* dev_status, hipStream_t stream);
 
 struct FlashArgs {
