@@ -22,6 +22,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float wave_sum(float v) {
 #pragma unroll
@@ -34,6 +35,11 @@ __device__ inline float wave_max(float v) {
     return v;
 }
 __device__ inline int wave_sum_i(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+__device__ inline uint32_t wave_sum_u(uint32_t v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
     return v;
@@ -127,7 +133,10 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * RPW + slot;
-            raw[u] = r < len ? *(reinterpret_cast<const uint4*>(src + int64_t(r) * D) + ch) : make_uint4(0, 0, 0, 0);
+            // streamed once: nontemporal, so the block rows do not displace cached data
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + int64_t(min(r, len - 1)) * D) + ch;
+            const u32x4 v = __builtin_nontemporal_load(p);
+            raw[u] = r < len ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -200,17 +209,24 @@ __device__ inline RowGeom row_geom(const TopCdfArgs& a, int i) {
     return g;
 }
 
-__device__ inline bool forced_block(const TopCdfArgs& a, const RowGeom& g, int j, float sk) {
+// Forcing that does not depend on the query block: the similarity guard on
+// the key block and the sink ranges.
+__device__ inline bool column_forced(const TopCdfArgs& a, int j, float sk) {
     const int64_t k_first = int64_t(j) * a.bk;
     const int64_t k_end = min(k_first + a.bk, a.N);
     bool f = (a.theta > 0.f) && (sk < a.theta);
     f |= (a.sink_front > 0) && (k_first < a.sink_front);
     f |= (a.sink_back > 0) && (k_end > a.N - a.sink_back);
-    if (a.causal) {
-        f |= (a.window > 0) && (k_end - 1 >= g.q_first - a.window + 1);
-        f |= (k_first < g.q_end) && (k_end > g.q_first);
-    }
     return f;
+}
+
+// Causal forcing of key block j for a query block: its sliding window and
+// the diagonal block(s) it overlaps.
+__device__ inline bool causal_forced(const TopCdfArgs& a, const RowGeom& g, int j) {
+    const int64_t k_first = int64_t(j) * a.bk;
+    const int64_t k_end = min(k_first + a.bk, a.N);
+    return ((a.window > 0) && (k_end - 1 >= g.q_first - a.window + 1)) ||
+           ((k_first < g.q_end) && (k_end > g.q_first));
 }
 
 // Probabilities in fixed point: P = floor(p * 2^31).  The candidates'
@@ -220,232 +236,273 @@ __device__ inline bool forced_block(const TopCdfArgs& a, const RowGeom& g, int j
 constexpr float kFix = 2147483648.0f;
 constexpr double kFixD = 2147483648.0;
 
-// Radix digits of the selection keys (probability bits + 1 < 2^30):
-// bits 29..22, 21..14, 13..6, 5..0.
+// Selection key of a candidate: its probability bits + 1 (so 0 < key < 2^30,
+// ordered like the probability); 0 marks a block that is not a candidate and
+// kForcedKey a forced one.  P is a function of the key.
+constexpr uint32_t kForcedKey = 0x80000000u;
+__device__ inline uint32_t key_mass(uint32_t key) { return uint32_t(__uint_as_float(key - 1u) * kFix); }
+__device__ inline bool is_candidate(uint32_t key) { return key != 0u && key < kForcedKey; }
+
+// Radix digits of the keys: bits 29..22, 21..14, 13..6, 5..0.
 __device__ inline int digit_shift(int lv) { return lv == 3 ? 0 : 22 - 8 * lv; }
 __device__ inline int digit_width(int lv) { return lv == 3 ? 6 : 8; }
 
 // In the histogram scan lane l owns digits 255-4l .. 252-4l (highest first).
 // Finds the first digit, in descending order, at which base + the inclusive
-// cumulative value reaches `target`; returns false when none does.
-// val(x) extracts the scanned quantity from a bin, cnt(x) the bin count.
-struct ScanHit {
-    uint32_t digit, before, count_before, bin_count;
-};
-
-template <typename Val, typename Cnt>
-__device__ inline bool scan_digits(const uint32_t (&vb)[4], const uint32_t (&cb)[4], uint32_t base,
-                                   uint32_t target, int lane, Val val, Cnt cnt, ScanHit& out) {
-    uint32_t lv = 0, lc = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        lv += val(vb[t]);
-        lc += cnt(cb[t]);
-    }
-    const uint32_t iv = wave_incl_scan(lv);
-    const uint32_t ic = wave_incl_scan(lc);
-    const unsigned long long hit = __ballot(base + iv >= target);
+// cumulative bin value reaches `target`; returns false when none does, else
+// the digit and the cumulative value of the digits above it.
+__device__ inline bool scan_digits(const uint32_t* hist, uint32_t base, uint32_t target, int lane,
+                                   uint32_t& digit, uint32_t& before) {
+    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const uint32_t v[4] = {h4.w, h4.z, h4.y, h4.x};  // descending digits
+    const uint32_t lt = v[0] + v[1] + v[2] + v[3];
+    const uint32_t incl = wave_incl_scan(lt);
+    const unsigned long long hit = __ballot(base + incl >= target);
     if (hit == 0ull) return false;
     const int hl = __ffsll(static_cast<long long>(hit)) - 1;
-    uint32_t run = iv - lv, runc = ic - lc;
-    uint32_t pos = 3, bef = run, befc = runc, bc = 0;
+    uint32_t run = incl - lt, pos = 3, bef = run;
     bool done = false;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        if (!done && base + run + val(vb[t]) >= target) {
+        if (!done && base + run + v[t] >= target) {
             pos = t;
             bef = run;
-            befc = runc;
-            bc = cnt(cb[t]);
             done = true;
         }
-        run += val(vb[t]);
-        runc += cnt(cb[t]);
+        run += v[t];
     }
-    const uint32_t dg = 255u - 4u * uint32_t(lane) - pos;
-    out.digit = __builtin_amdgcn_readlane(dg, hl);
-    out.before = __builtin_amdgcn_readlane(bef, hl);
-    out.count_before = __builtin_amdgcn_readlane(befc, hl);
-    out.bin_count = __builtin_amdgcn_readlane(bc, hl);
+    digit = __builtin_amdgcn_readlane(255u - 4u * uint32_t(lane) - pos, hl);
+    before = __builtin_amdgcn_readlane(bef, hl);
     return true;
 }
 
-// One query block (row i of head bh) on one wavefront.  Element r of lane l is
-// key block j = 64 r + l.  Candidates are ordered by probability descending,
-// ties by block index ascending; TopCdf keeps the shortest prefix whose mass
-// reaches tau, the floor keeps at least `extra` candidates.  Both cut points
-// are found exactly with four histogram passes over the radix digits of the
-// probability bits (the TopCdf search carries the mass per bin, the floor
-// search the count), so no sort is needed.  Returns the row's kept count.
-template <int EPL>
-__device__ int select_row(const TopCdfArgs& a, int bh, int i, const float* lrow, const float* simk,
-                          uint32_t* hCX, uint32_t* hS, int lane) {
-    const RowGeom g = row_geom(a, i);
-    const int64_t row = int64_t(bh) * a.n_qb + i;
-    const bool forced_row = a.theta > 0.f && a.simq[row] < a.theta;
-
-    float e[EPL];
-    uint32_t fbits = 0, cbits = 0;
-    float cmax = -FLT_MAX;
+// Histogram of digit `lv` over the candidate keys that carry prefix `pref`
+// above it, in this wavefront's 256-bin LDS array: counts, or fixed-point
+// masses when MASS.
+template <bool MASS>
+__device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pref, uint32_t* hist, int lane) {
+    const int sh = digit_shift(lv), w = digit_width(lv);
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
+    wave_lds_sync();
+    for (int q = lane; 4 * q < nv; q += 64) {
+        const uint4 x = row4[q];
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-        e[r] = 0.f;
-        if (r * 64 < g.nv) {
-            const int j = r * 64 + lane;
-            if (j < g.nv) {
-                const float l = lrow[j];
-                e[r] = l;
-                if (forced_block(a, g, j, simk[j])) {
-                    fbits |= 1u << r;
-                } else {
-                    cbits |= 1u << r;
-                    cmax = fmaxf(cmax, l);
-                }
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
+            // forced keys never match a prefix
+            if (kk != 0u && (kk >> (sh + w)) == pref) {
+                const uint32_t d = (kk >> sh) & ((1u << w) - 1u);
+                atomicAdd(&hist[d], MASS ? key_mass(kk) : 1u);
             }
         }
     }
-    cmax = wave_max(cmax);
-    const int n_forced = wave_sum_i(__popc(fbits));
-    const int n_cand = wave_sum_i(__popc(cbits));
-    float esum = 0.f;
+    wave_lds_sync();
+}
+
+// One query block (row i of head bh) on one wavefront, its compressed scores
+// in `row` (LDS, 16-byte aligned; overwritten with the selection keys).  Each
+// lane takes four consecutive key blocks per step.  Candidates are ordered by
+// probability descending, ties by block index ascending; TopCdf keeps the
+// shortest prefix whose mass reaches tau, the floor keeps at least `extra`
+// candidates.  Both cut points are found exactly with four histogram passes
+// over the radix digits of the keys (the TopCdf search carries the mass per
+// bin, the floor search the count), so no sort is needed.  Returns the row's
+// kept count.
+__device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, const uint8_t* colf,
+                          uint32_t* hS, int lane) {
+    const RowGeom g = row_geom(a, i);
+    const int64_t grow = int64_t(bh) * a.n_qb + i;
+    const bool forced_row = a.theta > 0.f && a.simq[grow] < a.theta;
+    const int nv = g.nv;
+    uint4* row4 = reinterpret_cast<uint4*>(row);
+
+    // forcing and the candidates' maximum score
+    float cmax = -FLT_MAX;
+    int nf = 0, nc = 0;
+    for (int q = lane; 4 * q < nv; q += 64) {
+        uint4 x = row4[q];
+        uint32_t* xs = reinterpret_cast<uint32_t*>(&x);
+        const uint32_t cf = reinterpret_cast<const uint32_t*>(colf)[q];
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-        if ((cbits >> r) & 1u) {
-            e[r] = expf(e[r] - cmax);
-            esum += e[r];
+        for (int t = 0; t < 4; ++t) {
+            const int j = 4 * q + t;
+            if (j < nv) {
+                const bool f = ((cf >> (8 * t)) & 0xffu) || (a.causal && causal_forced(a, g, j));
+                if (f) {
+                    xs[t] = kForcedKey;
+                    ++nf;
+                } else {
+                    cmax = fmaxf(cmax, __uint_as_float(xs[t]));
+                    ++nc;
+                }
+            }
         }
+        row4[q] = x;
+    }
+    cmax = wave_max(cmax);
+    const int n_forced = wave_sum_i(nf);
+    const int n_cand = wave_sum_i(nc);
+    // softmax over the candidates, then the keys
+    float esum = 0.f;
+    for (int q = lane; 4 * q < nv; q += 64) {
+        uint4 x = row4[q];
+        uint32_t* xs = reinterpret_cast<uint32_t*>(&x);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (4 * q + t < nv && xs[t] != kForcedKey) {
+                const float ev = expf(__uint_as_float(xs[t]) - cmax);
+                xs[t] = __float_as_uint(ev);
+                esum += ev;
+            }
+        }
+        row4[q] = x;
     }
     esum = wave_sum(esum);
     const float inv_sum = 1.0f / esum;
-    uint32_t key[EPL], P[EPL];
+    for (int q = lane; 4 * q < nv; q += 64) {
+        uint4 x = row4[q];
+        uint32_t* xs = reinterpret_cast<uint32_t*>(&x);
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-        const bool c = (cbits >> r) & 1u;
-        const float p = c ? e[r] * inv_sum : 0.f;
-        key[r] = c ? __float_as_uint(p) + 1u : 0u;
-        P[r] = c ? uint32_t(p * kFix) : 0u;
+        for (int t = 0; t < 4; ++t)
+            if (4 * q + t < nv && xs[t] != kForcedKey) xs[t] = __float_as_uint(__uint_as_float(xs[t]) * inv_sum) + 1u;
+        row4[q] = x;
     }
 
+    int extra = 0;
+    if (a.sparsity >= 0.0) extra = max(0, int(ceil((1.0 - a.sparsity) * double(nv))) - n_forced);
     int k_cdf = 0;
-    bool c_on = false, c_all = false;
+    bool c_on = false;
     uint32_t T = 0;
     if (a.tau_d >= 1.0) {
         k_cdf = n_cand;
-    } else if (a.tau_d > 0.0 && n_cand > 0) {
+    } else if (a.tau_d > 0.0 && n_cand > 0 && extra < n_cand) {
         c_on = true;
         T = max(1u, uint32_t(ceil(a.tau_d * kFixD)));
     }
-    int extra = 0;
-    if (a.sparsity >= 0.0) extra = max(0, int(ceil((1.0 - a.sparsity) * double(g.nv))) - n_forced);
-    bool x_on = extra > 0 && extra < n_cand;
-    uint32_t c_pref = 0, c_acc = 0, c_cnt = 0, c_grp = 0;
+    // floor: the extra-th largest key and how many of its ties are needed
     uint32_t x_pref = 0, x_rem = uint32_t(extra);
-
-    for (int lv = 0; lv < 4 && (c_on || x_on); ++lv) {
-        const int sh = digit_shift(lv), w = digit_width(lv);
-        reinterpret_cast<uint4*>(hCX)[lane] = make_uint4(0, 0, 0, 0);
-        reinterpret_cast<uint4*>(hS)[lane] = make_uint4(0, 0, 0, 0);
-        wave_lds_sync();
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) {
-            if (r * 64 < g.nv) {
-                const uint32_t kk = key[r];
-                const uint32_t hi = kk >> (sh + w);
-                const uint32_t d = (kk >> sh) & ((1u << w) - 1u);
-                const bool mc = c_on && kk != 0u && hi == c_pref;
-                const bool mx = x_on && kk != 0u && hi == x_pref;
-                if (mc || mx) atomicAdd(&hCX[d], (mc ? 1u : 0u) + (mx ? 65536u : 0u));
-                if (mc) atomicAdd(&hS[d], P[r]);
-            }
+    const bool x_on = extra > 0 && extra < n_cand;
+    if (x_on) {
+        for (int lv = 0; lv < 4; ++lv) {
+            digit_hist<false>(row4, nv, lv, x_pref, hS, lane);
+            uint32_t d = 0, bef = 0;
+            scan_digits(hS, 0u, x_rem, lane, d, bef);
+            x_rem -= bef;
+            x_pref = (x_pref << digit_width(lv)) | d;
         }
-        wave_lds_sync();
-        const uint4 cx4 = reinterpret_cast<const uint4*>(hCX)[63 - lane];
-        const uint4 s4 = reinterpret_cast<const uint4*>(hS)[63 - lane];
-        const uint32_t cx[4] = {cx4.w, cx4.z, cx4.y, cx4.x};  // descending digits
-        const uint32_t sv[4] = {s4.w, s4.z, s4.y, s4.x};
         if (c_on) {
-            ScanHit h;
-            const bool found = scan_digits(sv, cx, c_acc, T, lane, [](uint32_t x) { return x; },
-                                           [](uint32_t x) { return x & 0xffffu; }, h);
-            if (!found) {  // the candidates' whole mass stays below tau (first level only)
-                c_on = false;
-                c_all = true;
-            } else {
-                c_acc += h.before;
-                c_cnt += h.count_before;
-                c_pref = (c_pref << w) | h.digit;
-                c_grp = h.bin_count;
+            // when the floor's candidates already hold tau of the mass, the
+            // TopCdf prefix is no longer than the floor
+            uint32_t m = 0;
+            for (int q = lane; 4 * q < nv; q += 64) {
+                const uint4 x = row4[q];
+                const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
+                    if (is_candidate(kk) && kk > x_pref) m += key_mass(kk);
+                }
             }
-        }
-        if (x_on) {
-            ScanHit h;
-            scan_digits(cx, cx, 0u, x_rem, lane, [](uint32_t x) { return x >> 16; },
-                        [](uint32_t x) { return x >> 16; }, h);
-            x_rem -= h.before;
-            x_pref = (x_pref << w) | h.digit;
+            m = wave_sum_u(m);
+            if (m + x_rem * key_mass(x_pref) >= T) c_on = false;
         }
     }
+    // TopCdf: the key at which the cumulative mass reaches tau
+    uint32_t c_pref = 0, c_cnt = 0;
     if (c_on) {
-        // c_pref is the key at which the cumulative mass reaches tau; it is
-        // shared by c_grp candidates of equal P, taken in index order
-        const uint32_t Pv = uint32_t(__uint_as_float(c_pref - 1u) * kFix);
-        const uint32_t need = T - c_acc;
-        uint32_t m = Pv ? (need - 1u) / Pv : c_grp - 1u;
-        m = min(m, c_grp - 1u);
-        k_cdf = int(c_cnt + m + 1u);
-    } else if (c_all) {
-        k_cdf = n_cand;
+        uint32_t c_acc = 0;
+        bool found = true;
+        for (int lv = 0; lv < 4 && found; ++lv) {
+            digit_hist<true>(row4, nv, lv, c_pref, hS, lane);
+            uint32_t d = 0, bef = 0;
+            found = scan_digits(hS, c_acc, T, lane, d, bef);
+            c_acc += bef;
+            c_pref = (c_pref << digit_width(lv)) | d;
+        }
+        if (!found) {  // the candidates' whole mass stays below tau
+            k_cdf = n_cand;
+        } else {
+            // the key is shared by `grp` candidates of equal mass, taken in
+            // index order; `c_cnt` candidates rank above it
+            uint32_t above = 0, grp = 0;
+            for (int q = lane; 4 * q < nv; q += 64) {
+                const uint4 x = row4[q];
+                const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
+                    above += (is_candidate(kk) && kk > c_pref) ? 1u : 0u;
+                    grp += kk == c_pref ? 1u : 0u;
+                }
+            }
+            c_cnt = wave_sum_u(above);
+            grp = wave_sum_u(grp);
+            const uint32_t Pv = key_mass(c_pref);
+            const uint32_t need = T - c_acc;
+            uint32_t m = Pv ? (need - 1u) / Pv : grp - 1u;
+            m = min(m, grp - 1u);
+            k_cdf = int(c_cnt + m + 1u);
+        }
     }
     const int keep = min(n_cand, max(k_cdf, extra));
 
-    uint32_t kbits = 0;
-    if (!forced_row && keep > 0) {
-        if (keep == n_cand) {
-            kbits = cbits;
-        } else {
-            uint32_t v_thr, quota;
-            if (keep == k_cdf) {
-                v_thr = c_pref;
-                quota = uint32_t(k_cdf) - c_cnt;
-            } else {
-                v_thr = x_pref;
-                quota = x_rem;
-            }
-            const unsigned long long below = (1ull << lane) - 1ull;
-            uint32_t run = 0;
+    // threshold key and how many of its ties (lowest indices first) are kept
+    uint32_t v_thr = 0xffffffffu, quota = 0;
+    if (forced_row || keep == 0) {
+        v_thr = 0xffffffffu;  // no candidate passes
+    } else if (keep == n_cand) {
+        v_thr = 0u;  // every candidate passes
+    } else if (keep == k_cdf) {
+        v_thr = c_pref;
+        quota = uint32_t(k_cdf) - c_cnt;
+    } else {
+        v_thr = x_pref;
+        quota = x_rem;
+    }
+    uint8_t* out = a.mask + grow * a.n_kb;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    uint32_t run = 0;
+    for (int q0 = 0; 4 * q0 < a.n_kb; q0 += 64) {
+        const int q = q0 + lane;
+        const uint4 x = 4 * q < nv ? row4[q] : make_uint4(0, 0, 0, 0);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+        bool cand[4], eq[4];
+        unsigned long long em[4];
+        uint32_t before = run;
 #pragma unroll
-            for (int r = 0; r < EPL; ++r) {
-                if (r * 64 < g.nv) {
-                    const bool gt = key[r] > v_thr;
-                    const bool eq = key[r] == v_thr;
-                    const unsigned long long eqm = __ballot(eq);
-                    const uint32_t rank = run + uint32_t(__popcll(eqm & below));
-                    if (gt || (eq && rank < quota)) kbits |= 1u << r;
-                    run += uint32_t(__popcll(eqm));
-                }
-            }
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
+            cand[t] = is_candidate(kk);
+            eq[t] = cand[t] && kk == v_thr;
+            em[t] = __ballot(eq[t]);
+            before += uint32_t(__popcll(em[t] & below));
+        }
+        uint32_t rank = before;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int j = 4 * q + t;
+            const uint32_t kk = j < nv ? xs[t] : 0u;
+            const bool kept = cand[t] && (kk > v_thr || (eq[t] && rank < quota));
+            if (eq[t]) ++rank;
+            if (j < a.n_kb) out[j] = forced_row ? uint8_t(j < nv) : uint8_t(kk == kForcedKey || kept);
+            run += uint32_t(__popcll(em[t]));
         }
     }
-    uint8_t* out = a.mask + row * a.n_kb;
-    const uint32_t bits = fbits | kbits;
-#pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-        const int j = r * 64 + lane;
-        if (r * 64 < a.n_kb && j < a.n_kb) out[j] = forced_row ? uint8_t(j < g.nv) : uint8_t((bits >> r) & 1u);
-    }
-    const int cnt = forced_row ? g.nv : n_forced + keep;
-    if (lane == 0) a.counts[row] = cnt;
+    const int cnt = forced_row ? nv : n_forced + keep;
+    if (lane == 0) a.counts[grow] = cnt;
     return cnt;
 }
 
-// Dynamic LDS: scores[16][ls] f32 | per wave: counts[256] u32 (TopCdf search
-// in the low half, floor search in the high half) and masses[256] u32.
-template <int D, int EPL>
+// Dynamic LDS: scores[16][ls] f32 | per wave: histogram[256] u32 | column
+// forcing flags[n_kb] u8.
+template <int D>
 __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int32_t wave_tot[4];
     float* scores = reinterpret_cast<float*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(scores + kGroupRows * ls);
+    uint8_t* colf = reinterpret_cast<uint8_t*>(hist + 4 * 256);
 
     const int groups = (a.n_qb + kGroupRows - 1) / kGroupRows;
     const int bh = blockIdx.x / groups;  // b * Hq + hq
@@ -461,11 +518,15 @@ __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
     const int i_last = min(i0 + kGroupRows, a.n_qb) - 1;
     const int ncols = row_geom(a, i_last).nv;  // columns any row of the group can see
 
+    for (int j = threadIdx.x; j < ncols; j += 256) colf[j] = column_forced(a, j, simk[j]) ? 1 : 0;
+
     // ---- compressed scores on v_mfma_f32_16x16x4_f32: A = 16 key-block means
     // (rows), B = the group's 16 query-block means (columns).  Lane l feeds
     // operand slot l/16 of row/column l%16; head-dim entry 16c + 4(l/16) + e
     // goes to step (c, e), so each lane reads float4s of contiguous entries.
     // The result lands as query row l%16, key blocks 4(l/16)..+3 of the tile.
+    // Tiles t and t+4 of a wave alternate between two register buffers, so
+    // the next tile's loads are in flight during the current tile's MFMAs.
     {
         constexpr int C = D / 16;
         const int r16 = lane & 15;
@@ -475,39 +536,43 @@ __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
 #pragma unroll
         for (int c = 0; c < C; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qs + 16 * c);
         const int ntile = (ncols + 15) >> 4;
-        f32x4 kv[C];
-        auto load_k = [&](int t) {
+        auto load_k = [&](f32x4 (&kv)[C], int t) {
             const float* ks = kbar + int64_t(min(t * 16 + r16, ncols - 1)) * D + 4 * sub;
 #pragma unroll
             for (int c = 0; c < C; ++c) kv[c] = *reinterpret_cast<const f32x4*>(ks + 16 * c);
         };
-        if (wave < ntile) load_k(wave);
-        for (int t = wave; t < ntile; t += 4) {
-            f32x4 kc[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) kc[c] = kv[c];
-            if (t + 4 < ntile) load_k(t + 4);
+        auto tile = [&](const f32x4 (&kv)[C], int t) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < C; c += 2)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[c][e], qv[c][e], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[c + 1][e], qv[c + 1][e], acc1, 0, 0, 0);
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c][e], qv[c][e], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c + 1][e], qv[c + 1][e], acc1, 0, 0, 0);
                 }
             const f32x4 s = (acc0 + acc1) * a.scale;
             *reinterpret_cast<f32x4*>(scores + r16 * ls + t * 16 + 4 * sub) = s;
+        };
+        f32x4 ka[C], kb[C];
+        if (wave < ntile) load_k(ka, wave);
+        if (wave + 4 < ntile) load_k(kb, wave + 4);
+        for (int t = wave; t < ntile; t += 8) {
+            tile(ka, t);
+            if (t + 8 < ntile) load_k(ka, t + 8);
+            if (t + 4 < ntile) {
+                tile(kb, t + 4);
+                if (t + 12 < ntile) load_k(kb, t + 12);
+            }
         }
     }
     __syncthreads();
 
-    uint32_t* hCX = hist + wave * 512;
-    uint32_t* hS = hCX + 256;
+    uint32_t* hS = hist + wave * 256;
     int tot = 0;
     for (int rr = wave; rr < kGroupRows; rr += 4) {
         const int i = i0 + rr;
         if (i >= a.n_qb) break;
-        tot += select_row<EPL>(a, bh, i, scores + rr * ls, simk, hCX, hS, lane);
+        tot += select_row(a, bh, i, reinterpret_cast<uint32_t*>(scores + rr * ls), colf, hS, lane);
     }
     if (lane == 0) wave_tot[wave] = tot;
     __syncthreads();
@@ -609,21 +674,6 @@ __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, c
     }
 }
 
-template <int D, int EPL>
-hipError_t launch_topcdf_t(const TopCdfArgs& a, unsigned nwg, size_t lds, int ls, hipStream_t stream) {
-    hipLaunchKernelGGL((k_topcdf<D, EPL>), dim3(nwg), dim3(256), lds, stream, a, ls);
-    return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_topcdf_d(const TopCdfArgs& a, unsigned nwg, size_t lds, int ls, hipStream_t stream) {
-    if (a.n_kb <= 64) return launch_topcdf_t<D, 1>(a, nwg, lds, ls, stream);
-    if (a.n_kb <= 256) return launch_topcdf_t<D, 4>(a, nwg, lds, ls, stream);
-    if (a.n_kb <= 512) return launch_topcdf_t<D, 8>(a, nwg, lds, ls, stream);
-    if (a.n_kb <= 1024) return launch_topcdf_t<D, 16>(a, nwg, lds, ls, stream);
-    return launch_topcdf_t<D, 32>(a, nwg, lds, ls, stream);
-}
-
 }  // namespace
 
 int64_t topcdf_groups(int64_t bh, int64_t n_qb) { return bh * ((n_qb + kGroupRows - 1) / kGroupRows); }
@@ -648,12 +698,15 @@ hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Predic
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream) {
     if (a.n_kb > SA_MAX_KEY_BLOCKS) return hipErrorInvalidValue;
     const int ls = score_stride(a.n_kb);
-    const size_t lds = size_t(kGroupRows) * ls * 4 + size_t(4) * 512 * 4;
+    const size_t lds = size_t(kGroupRows) * ls * 4 + size_t(4) * 256 * 4 + size_t(a.n_kb + 15) / 16 * 16;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t nwg = topcdf_groups(int64_t(a.B) * a.Hq, a.n_qb);
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
-    if (a.D == 128) return launch_topcdf_d<128>(a, unsigned(nwg), lds, ls, stream);
-    return launch_topcdf_d<64>(a, unsigned(nwg), lds, ls, stream);
+    if (a.D == 128)
+        hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), dim3(256), lds, stream, a, ls);
+    else
+        hipLaunchKernelGGL(k_topcdf<64>, dim3(unsigned(nwg)), dim3(256), lds, stream, a, ls);
+    return hipGetLastError();
 }
 
 hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t* group_tot, int64_t bh,
