@@ -19,6 +19,7 @@
 //
 // k_flash_small<D>: the 16x16-block case (tiny workloads), plain fp32 ALU.
 #include <cmath>
+#include <type_traits>
 
 #include "sa_internal.h"
 
@@ -272,6 +273,11 @@ __device__ inline float max3f(float a, float b, float c) {
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
 }
+__device__ inline float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 // (value of this lane, value of lane ^ 32) combined: returns both halves' values
 __device__ inline void swap32(float v, float& lo, float& hi) {
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -291,23 +297,60 @@ __device__ inline float max_lanes32(float v) {
 
 // DMA variant (the production path for 64-key tiles).  K and V tiles go
 // straight from HBM/L2 into LDS with buffer_load ... lds (16 bytes per lane,
-// rows past the sequence end read as zero), double-buffered: the DMA of tile
-// t+1 runs while tile t is computed, one vmcnt wait + barrier per tile.
-// Each 1 KB DMA instruction moves 8 rows x 128 bytes (whole cache lines); in
-// LDS the 16-byte chunks of row r are XOR-permuted (K: by (r>>1)&7, V: by
-// r&7) so that the MFMA operand reads are bank-conflict free: the K operand
-// (ds_read_b128, key row 32mt+(l&31), head-dim chunk 2ks+(l>>5)) and the
-// transposed V operand (ds_read_b64_tr_b16: in each 16-lane group lane i slot
-// j receives element i&3 of the 8 bytes lane 4j+i/4 read, so lane l reads
+// rows past the sequence end read as zero).  Each 1 KB DMA instruction moves
+// 8 rows x 128 bytes (whole cache lines); in LDS the 16-byte chunks of row r
+// are XOR-permuted (K: by (r>>1)&7, V: by r&7) so that the MFMA operand reads
+// are bank-conflict free: the K operand (ds_read_b128, key row 32mt+(l&31),
+// head-dim chunk 2ks+(l>>5)) and the transposed V operand (ds_read_b64_tr_b16:
+// in each 16-lane group lane i slot j receives element i&3 of the 8 bytes
+// lane 4j+i/4 read, so lane l reads
 // V[16ps + 8ab + 4(l>>5) + ((l&15)>>2)][32tt + 16((l>>4)&1) + 4(l&3) .. +3]).
 // All read addresses are one of a few per-lane offsets plus an immediate.
+//
+// With PV skip on (LAM) most tiles never need V: K runs two tiles ahead in
+// three LDS buffers, and V is fetched only by a wavefront that runs the PV
+// product of the tile, into a single buffer (all waves sit in the same tile
+// between barriers).  Without PV skip, K and V run one tile ahead in two
+// buffers each.  The skip test of a 32-row group is one ballot: skip when no
+// valid row's block maximum comes within lambda of its new running maximum.
+//
+// The exponentials are taken against the running maximum itself, so the
+// largest probability of the row is exactly 1 (exact in bf16 for the PV
+// product); O and l are rescaled only on tiles where some row's maximum rises.
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from buffer `r` at byte offset `off` into LDS at dst + 16*lane
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+// Workgroup barrier without the implied memory waits: the caller has already
+// waited for what must be complete (the in-flight DMA of a later tile is not
+// waited for); the clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ inline void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer resource (descriptor words) over one head's rows, for the DMA below.
+typedef int int4v __attribute__((ext_vector_type(4)));
+__device__ inline int4v head_desc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return int4v{int(uint32_t(p)), int(uint32_t(p >> 32) & 0xffff), int(bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer `r` at byte offset `off` into LDS at dst + 16*lane.
+// Issued as assembly so the compiler does not track it: it would otherwise
+// wait for every outstanding LDS DMA before any LDS read.  The kernels wait
+// explicitly (dma_wait) before reading a DMA'd buffer.
+__device__ inline void dma16(int4v r, const uint16_t* dst, uint32_t off) {
+    const uint32_t la = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)dst));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(la), "v"(off), "s"(r) : "memory", "m0");
+}
+// vmcnt(N): at most N of this wave's vector memory operations outstanding
+template <int N>
+__device__ inline void dma_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else static_assert(N == 0 || N == 2 || N == 4, "add the count");
 }
 
 template <int D, int SUB, bool LAM>
@@ -320,8 +363,23 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int KS = D / 16;               // MFMA k-steps over the head dim
     constexpr int SEG = D / 64;              // 128-byte segments per row
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
-    __shared__ __align__(16) uint16_t Ks[2][BK * D];
-    __shared__ __align__(16) uint16_t Vs[2][BK * D];
+    // One array per buffer, selected at compile time: the compiler can then
+    // prove that a DMA into one buffer does not alias operand reads from
+    // another and does not wait for it.
+    __shared__ __align__(16) uint16_t Ks0[BK * D];
+    __shared__ __align__(16) uint16_t Ks1[BK * D];
+    __shared__ __align__(16) uint16_t Ks2[LAM ? BK * D : 8];
+    __shared__ __align__(16) uint16_t Vs0[BK * D];
+    __shared__ __align__(16) uint16_t Vs1[LAM ? 8 : BK * D];
+    auto kbuf_of = [&](auto I) -> uint16_t* {
+        if constexpr (decltype(I)::value == 0) return Ks0;
+        else if constexpr (decltype(I)::value == 1) return Ks1;
+        else return Ks2;
+    };
+    auto vbuf_of = [&](auto I) -> uint16_t* {
+        if constexpr (decltype(I)::value == 0) return Vs0;
+        else return Vs1;
+    };
 
     const int G = a.B * a.Hq * a.n_qb;
     const int per = (G + 7) >> 3;
@@ -334,8 +392,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int hk = hq / (a.Hq / a.Hkv);
     const int N = int(a.N);
     const uint32_t head_bytes = uint32_t(N) * D * 2u;
-    const __amdgpu_buffer_rsrc_t rK = head_rsrc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rV = head_rsrc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -378,24 +436,24 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         const int rg = idx / SEG, seg = idx % SEG;
         return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
     };
-    auto issue_k = [&](int kb0, int buf) {
+    auto issue_k = [&](int kb0, uint16_t* dst) {
 #pragma unroll
         for (int c = 0; c < DI; ++c) {
             const int idx = wave * DI + c;
-            dma16(rK, &Ks[buf][idx * 512], k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+            dma16(rK, dst + idx * 512, k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
         }
     };
-    auto issue_v = [&](int kb0, int buf) {  // this wave's share of the V tile
+    auto issue_v = [&](int kb0, uint16_t* dst) {  // this wave's share of the V tile
 #pragma unroll
         for (int c = 0; c < DI; ++c) {
             const int idx = wave * DI + c;
-            dma16(rV, &Vs[buf][idx * 512], v_lane + tile_base(kb0, idx));
+            dma16(rV, dst + idx * 512, v_lane + tile_base(kb0, idx));
         }
     };
-    auto issue_v_all = [&](int kb0, int buf) {  // the whole V tile by this wave alone
+    auto issue_v_all = [&](int kb0) {  // the whole V tile by this wave alone
 #pragma unroll 1
         for (int idx = 0; idx < 4 * DI; ++idx)
-            dma16(rV, &Vs[buf][idx * 512], v_lane + tile_base(kb0, idx));
+            dma16(rV, Vs0 + idx * 512, v_lane + tile_base(kb0, idx));
     };
     // operand read offsets (elements): K for ks % 4, V for tt % 2
     int k_off[4], v_off[2];
@@ -408,9 +466,6 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         for (int x = 0; x < 2; ++x)
             v_off[x] = ((4 * half + j) * 128 + (((4 * x + 2 * g + (m >> 1)) ^ (4 * half + j)) * 16) + 8 * (m & 1)) / 2;
     }
-    // PV-skip bookkeeping: need[t & 1][w] = wave w ran the PV product of tile t
-    __shared__ int need[2][4];
-    int v_ready = 3;  // bit b: the V tile of LDS buffer b was fetched
 
     floatx16 oacc[NT];
 #pragma unroll
@@ -424,33 +479,25 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     int n_exec = 0, n_skip = 0;
     bool bad_col = false;
 
-    if (nt > 0) {
-        issue_k(tile_key0(0), 0);
-        issue_v(tile_key0(0), 0);
-    }
-    if (lane == 0) need[1][wave] = 1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
+    // tile t: K in buffer KC; DMA target of the next K (t+2 with PV skip, t+1
+    // without) is buffer KN; without PV skip V of tile t is in buffer KC too
+    auto step = [&](int t, auto KC, auto KN) {
         const int kb0 = tile_key0(t);
-        if (t + 1 < nt) {
-            const int kn = tile_key0(t + 1);
-            issue_k(kn, buf ^ 1);
-            // with PV skip on, V of the next tile is fetched only if some wave
-            // ran the PV product of the previous tile (runs of skips are long)
-            bool want_v = true;
-            if constexpr (LAM) want_v = (need[buf ^ 1][0] | need[buf ^ 1][1] | need[buf ^ 1][2] | need[buf ^ 1][3]) != 0;
-            if (want_v) issue_v(kn, buf ^ 1);
-            v_ready = want_v ? (v_ready | (2 >> buf)) : (v_ready & ~(2 >> buf));
+        if constexpr (LAM) {
+            if (t + 2 < nt) issue_k(tile_key0(t + 2), kbuf_of(KN));
+        } else {
+            if (t + 1 < nt) {
+                const int kn = tile_key0(t + 1);
+                issue_k(kn, kbuf_of(KN));
+                issue_v(kn, vbuf_of(KN));
+            }
         }
-        int my_need = 0;
         if (kb0 < 0) {
             bad_col = true;
         } else if (!wave_rows) {
             if (LAM && pv_skip && lane == 0 && t % SUB == 0) pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
         } else {
-            const uint16_t* K = Ks[buf];
+            const uint16_t* K = kbuf_of(KC);
             floatx16 s0, s1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
@@ -462,8 +509,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
-            const bool need_mask = (kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0);
-            if (need_mask) {
+            if ((kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = kb0 + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -478,50 +524,51 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             for (int r = 0; r < 4; ++r) {
                 const float m1 = max3f(s0[4 * r], s0[4 * r + 1], s0[4 * r + 2]);
                 const float m2 = max3f(s0[4 * r + 3], s1[4 * r], s1[4 * r + 1]);
-                mx[r] = max3f(m1, m2, fmaxf(s1[4 * r + 2], s1[4 * r + 3]));
+                mx[r] = max3f(m1, m2, max2f(s1[4 * r + 2], s1[4 * r + 3]));
             }
             float lo, hi;
-            swap32(max3f(mx[0], mx[1], fmaxf(mx[2], mx[3])), lo, hi);
-            const float smax = fmaxf(lo, hi);
-            const float m_new = fmaxf(m_run, smax);
+            swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
+            const float smax = max2f(lo, hi);
+            const float m_new = max2f(m_run, smax);
             bool skip = false;
             if constexpr (LAM) {
-                const float gap = (row_valid && smax > -INFINITY) ? smax - m_new : -INFINITY;
-                skip = max_lanes32(gap) < lam_raw;
+                // NaN (no key yet) and -inf gaps never reach lambda
+                skip = __builtin_amdgcn_ballot_w64(row_valid && smax - m_new >= lam_raw) == 0ull;
             }
-            const float msafe = m_new == -INFINITY ? 0.f : m_new;
-            const float mc = msafe * c2;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - msafe) * c2);
-            float ps0 = 0.f, ps1 = 0.f;
+            // a skipped tile never raises a valid row's maximum, so O and l
+            // are rescaled here only on tiles that also run their PV product
+            if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);  // 0 when m_run = -inf
+                l_part *= alpha;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[tt][i] *= alpha;
+            }
+            m_run = m_new;
+            const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
-                s0[i] = p0;
-                s1[i] = p1;
-                ps0 += p0;
-                ps1 += p1;
+                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
+                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
             }
-            l_part = fmaf(l_part, alpha, ps0 + ps1);
-            m_run = m_new;
+            float ps[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
+            l_part += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
             if (LAM && pv_skip && lane == 0 && t % SUB == 0)
                 pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
             if (skip) {
                 ++n_skip;
             } else {
                 ++n_exec;
-                my_need = 1;
-                if (LAM && !((v_ready >> buf) & 1)) {
-                    // not prefetched: fetch the whole tile now (other waves may do the
-                    // same concurrently; they write identical bytes)
-                    issue_v_all(kb0, buf);
-                    __builtin_amdgcn_s_waitcnt(0);
-                }
-                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) oacc[tt][i] *= alpha;
+                const uint16_t* Vt = vbuf_of(KC);
+                if constexpr (LAM) {
+                    // fetch the tile now (other waves may do the same concurrently;
+                    // they write identical bytes)
+                    issue_v_all(kb0);
+                    dma_wait<0>();
+                    Vt = Vs0;
                 }
                 bf16x8_t pb[4];
 #pragma unroll
@@ -534,19 +581,51 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-                    for (int ps = 0; ps < 4; ++ps) {
-                        const uint16_t* pa = Vs[buf] + v_off[tt & 1] + ((2 * ps) * SEG + (tt >> 1)) * 512;
+                    for (int ps4 = 0; ps4 < 4; ++ps4) {
+                        const uint16_t* pa = Vt + v_off[tt & 1] + ((2 * ps4) * SEG + (tt >> 1)) * 512;
                         const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
                         const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(pa + SEG * 512));
                         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps], oacc[tt], 0, 0, 0);
+                        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps4], oacc[tt], 0, 0, 0);
                     }
                 }
             }
         }
-        if (lane == 0) need[buf][wave] = my_need;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for tile t+1 has landed
-        __syncthreads();                // ... and everyone's; buffer `buf` is free again
+        // the K tile of t+1 (and its V without PV skip) has landed; with PV skip
+        // the K tile of t+2 may still be in flight.  Operand reads of tile t
+        // are complete (consumed by the MFMAs).
+        if constexpr (LAM) {
+            if (t + 2 < nt) dma_wait<DI>();
+            else dma_wait<0>();
+        } else {
+            dma_wait<0>();
+        }
+        tile_barrier();  // ... and everyone's; the buffers of tile t are free again
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (nt > 0) {
+        issue_k(tile_key0(0), Ks0);
+        if constexpr (!LAM) issue_v(tile_key0(0), Vs0);
+    }
+    if constexpr (LAM) {
+        if (nt > 1) issue_k(tile_key0(1), Ks1);
+    }
+    dma_wait<0>();
+    __syncthreads();
+    if constexpr (LAM) {
+        for (int t = 0; t < nt; t += 3) {
+            step(t, I0{}, I2{});
+            if (t + 1 < nt) step(t + 1, I1{}, I0{});
+            if (t + 2 < nt) step(t + 2, I2{}, I1{});
+        }
+    } else {
+        for (int t = 0; t < nt; t += 2) {
+            step(t, I0{}, I1{});
+            if (t + 1 < nt) step(t + 1, I1{}, I0{});
+        }
     }
     if (!LAM && pv_skip && lane == 0)
         for (int e = e0; e < e1; ++e) pv_skip[int64_t(e) * 4 + wave] = 0;
