@@ -326,6 +326,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // waited for); the clobber keeps the compiler from moving memory accesses
 // across it.
 __device__ inline void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// this wave's LDS reads and writes are complete
+__device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Buffer resource (descriptor words) over one head's rows, for the DMA below.
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -339,9 +341,10 @@ __device__ inline int4v head_desc(const void* base, uint32_t bytes) {
 // wait for every outstanding LDS DMA before any LDS read.  The kernels wait
 // explicitly (dma_wait) before reading a DMA'd buffer.
 __device__ inline void dma16(int4v r, const uint16_t* dst, uint32_t off) {
-    const uint32_t la = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)dst));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(la), "v"(off), "s"(r) : "memory", "m0");
+    // the LDS address is wave-uniform; M0 is handed to the compiler as an operand
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)dst)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
 }
 // vmcnt(N): at most N of this wave's vector memory operations outstanding
 template <int N>
@@ -659,6 +662,288 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     }
 }
 
+// PV-skip variant of k_flash_dma (64-key tiles; the production path when
+// lambda is set).  Same LDS layouts, operand reads and online softmax.  The
+// PV product of a tile is deferred by one iteration: during iteration t the
+// four waves fetch V of tile t-1 cooperatively (only if some wave kept the PV
+// of that tile; the need flags come through LDS), while the scores and
+// softmax of tile t run; a barrier then lets the waves that kept it apply
+// O <- alpha O + P V for tile t-1.  O therefore lags one tile behind m and l;
+// a skipped tile never raises a valid row's maximum (its alpha is 1), so only
+// kept tiles carry a pending rescale.  K runs two tiles ahead in three
+// buffers; V needs one buffer.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                 uint8_t* __restrict__ pv_skip) {
+    constexpr int BQ = 128;
+    constexpr int BK = 64;
+    constexpr int NT = D / 32;               // 32-wide output column tiles
+    constexpr int KS = D / 16;               // MFMA k-steps over the head dim
+    constexpr int SEG = D / 64;              // 128-byte segments per row
+    constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
+    __shared__ __align__(16) uint16_t Ks[3][BK * D];
+    __shared__ __align__(16) uint16_t Vs[BK * D];
+    __shared__ int need[2][4];  // need[t & 1][w]: wave w keeps the PV product of tile t
+
+    const int G = a.B * a.Hq * a.n_qb;
+    const int per = (G + 7) >> 3;
+    const int row = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (row >= G) return;
+    const int qb = row % a.n_qb;
+    const int bh = row / a.n_qb;
+    const int hq = bh % a.Hq;
+    const int b = bh / a.Hq;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int N = int(a.N);
+    const uint32_t head_bytes = uint32_t(N) * D * 2u;
+    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int wrow0 = qb * BQ + wave * 32;
+    const int qrow = wrow0 + l32;
+    const bool row_valid = qrow < N;
+    const bool wave_rows = wrow0 < N;
+
+    bf16x8_t qf[KS];
+    {
+        const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qrow * D + ks * 16 + half * 8) * 2u));
+    }
+
+    const int e0 = row_ptr[row];
+    int e1 = row_ptr[row + 1];
+    if (e1 > a.col_cap) {
+        if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
+        e1 = int(a.col_cap);
+    }
+    const int nt = e1 > e0 ? e1 - e0 : 0;
+
+    auto tile_key0 = [&](int t) -> int {
+        const int j = col_idx[e0 + t];
+        if (j < 0 || j >= a.n_kb) return -1;
+        return j * BK;
+    };
+    // DMA: instruction idx covers rows 8*rg .. 8*rg+7 (rg = idx / SEG) of segment idx % SEG;
+    // lane L moves row 8*rg + L/8, LDS position L%8, i.e. source chunk (L%8) ^ swizzle(row)
+    const int dq = lane >> 3, dp = lane & 7;
+    const uint32_t k_lane[2] = {uint32_t(dq * D * 2 + ((dp ^ ((dq >> 1) & 7)) * 16)),
+                                uint32_t(dq * D * 2 + ((dp ^ ((4 + (dq >> 1)) & 7)) * 16))};
+    const uint32_t v_lane = uint32_t(dq * D * 2 + ((dp ^ dq) * 16));
+    auto tile_base = [&](int kb0, int idx) -> uint32_t {  // uniform part of the source offset
+        const int rg = idx / SEG, seg = idx % SEG;
+        return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
+    };
+    auto issue_k = [&](int kb0, int buf) {  // this wave's share of a K tile
+#pragma unroll
+        for (int c = 0; c < DI; ++c) {
+            const int idx = wave * DI + c;
+            dma16(rK, &Ks[buf][idx * 512], k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+        }
+    };
+    auto issue_v = [&](int kb0) {  // this wave's share of a V tile
+#pragma unroll
+        for (int c = 0; c < DI; ++c) {
+            const int idx = wave * DI + c;
+            dma16(rV, &Vs[idx * 512], v_lane + tile_base(kb0, idx));
+        }
+    };
+    // operand read offsets (elements): K for ks % 4, V for tt % 2
+    int k_off[4], v_off[2];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+        k_off[k4] = ((l32 >> 3) * SEG * 1024 + (l32 & 7) * 128 + (((2 * k4 + half) ^ ((l32 >> 1) & 7)) * 16)) / 2;
+    {
+        const int g = (lane >> 4) & 1, j = (lane & 15) >> 2, m = lane & 3;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            v_off[x] = ((4 * half + j) * 128 + (((4 * x + 2 * g + (m >> 1)) ^ (4 * half + j)) * 16) + 8 * (m & 1)) / 2;
+    }
+
+    floatx16 oacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
+    float m_run = -INFINITY;  // running max in raw score units (q.k)
+    float l_part = 0.f;
+    const float c2 = a.scale * kLog2e;
+    const float lam_raw = a.lambda / a.scale;
+    int n_exec = 0, n_skip = 0;
+    bool bad_col = false;
+    // the kept tile whose PV product is pending: P (bf16) and its rescale of O
+    bool pend = false;
+    bf16x8_t pp[4];
+    float palpha = 1.f;
+    auto apply_pending = [&]() {
+        if (__builtin_amdgcn_ballot_w64(palpha != 1.0f)) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[tt][i] *= palpha;
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+            for (int ps4 = 0; ps4 < 4; ++ps4) {
+                const uint16_t* pa = Vs + v_off[tt & 1] + ((2 * ps4) * SEG + (tt >> 1)) * 512;
+                const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
+                const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(pa + SEG * 512));
+                const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pp[ps4], oacc[tt], 0, 0, 0);
+            }
+        }
+    };
+    auto any_need = [&](int par) { return (need[par][0] | need[par][1] | need[par][2] | need[par][3]) != 0; };
+
+    if (nt > 0) issue_k(tile_key0(0), 0);
+    if (nt > 1) issue_k(tile_key0(1), 1);
+    dma_wait<0>();
+    __syncthreads();
+    int kbuf = 0;      // t % 3
+    int prev_kb0 = -1;  // first key of tile t-1
+    for (int t = 0; t < nt; ++t) {
+        const int kb0 = tile_key0(t);
+        // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
+        const bool vprev = t > 0 && any_need((t - 1) & 1);
+        if (vprev) issue_v(prev_kb0);
+        const bool kpre = t + 2 < nt;
+        if (kpre) issue_k(tile_key0(t + 2), kbuf == 0 ? 2 : kbuf - 1);
+
+        int my_need = 0;
+        float alpha = 1.f;
+        floatx16 s0, s1;
+        if (kb0 < 0) {
+            bad_col = true;
+        } else if (!wave_rows) {
+            if (pv_skip && lane == 0) pv_skip[int64_t(e0 + t) * 4 + wave] = 0;
+        } else {
+            const uint16_t* K = Ks[kbuf];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
+                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
+                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+            }
+            if ((kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kk = kb0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool ok0 = kk < N && (!a.causal || kk <= qrow);
+                    const bool ok1 = kk + 32 < N && (!a.causal || kk + 32 <= qrow);
+                    s0[i] = ok0 ? s0[i] : -INFINITY;
+                    s1[i] = ok1 ? s1[i] : -INFINITY;
+                }
+            }
+            float mx[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float m1 = max3f(s0[4 * r], s0[4 * r + 1], s0[4 * r + 2]);
+                const float m2 = max3f(s0[4 * r + 3], s1[4 * r], s1[4 * r + 1]);
+                mx[r] = max3f(m1, m2, max2f(s1[4 * r + 2], s1[4 * r + 3]));
+            }
+            float lo, hi;
+            swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
+            const float smax = max2f(lo, hi);
+            const float m_new = max2f(m_run, smax);
+            // NaN (no key yet) and -inf gaps never reach lambda
+            const bool skip = __builtin_amdgcn_ballot_w64(row_valid && smax - m_new >= lam_raw) == 0ull;
+            alpha = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;  // 0 when m_run = -inf
+            m_run = m_new;
+            const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
+                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
+            }
+            float ps[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
+            l_part = fmaf(l_part, alpha, ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
+            if (pv_skip && lane == 0) pv_skip[int64_t(e0 + t) * 4 + wave] = skip ? 1 : 0;
+            if (skip) {
+                ++n_skip;
+            } else {
+                ++n_exec;
+                my_need = 1;
+            }
+        }
+        // PV of tile t-1 once every wave's part of its V tile has landed
+        if (vprev) {
+            if (kpre) dma_wait<DI>();
+            else dma_wait<0>();
+            tile_barrier();
+            if (pend) apply_pending();
+        }
+        // tile t becomes the pending one
+        pend = my_need != 0;
+        if (pend) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                pp[0][x] = (__bf16)s0[x];
+                pp[1][x] = (__bf16)s0[8 + x];
+                pp[2][x] = (__bf16)s1[x];
+                pp[3][x] = (__bf16)s1[8 + x];
+            }
+            palpha = alpha;
+        }
+        if (lane == 0) need[t & 1][wave] = my_need;
+        // K of tile t+1 has landed (that of t+2 may be in flight); V reads and
+        // the need flags are complete
+        if (kpre) dma_wait<DI>();
+        else dma_wait<0>();
+        lds_wait();
+        tile_barrier();
+        prev_kb0 = kb0;
+        kbuf = kbuf == 2 ? 0 : kbuf + 1;
+    }
+    if (nt > 0 && any_need((nt - 1) & 1)) {
+        issue_v(prev_kb0);
+        dma_wait<0>();
+        tile_barrier();
+        if (pend) apply_pending();
+    }
+    if (bad_col && tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+
+    float l_lo, l_hi;
+    swap32(l_part, l_lo, l_hi);
+    const float l_tot = l_lo + l_hi;
+    if (row_valid) {
+        const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
+        if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
+        float* orow = a.o + int64_t(bh) * N * D + int64_t(qrow) * D;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float4 v;
+                v.x = oacc[tt][4 * g + 0] * inv;
+                v.y = oacc[tt][4 * g + 1] * inv;
+                v.z = oacc[tt][4 * g + 2] * inv;
+                v.w = oacc[tt][4 * g + 3] * inv;
+                *reinterpret_cast<float4*>(orow + 32 * tt + 8 * g + 4 * half) = v;
+            }
+    }
+    if (a.counters) {
+        if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)nt);
+        if (lane == 0 && wave_rows) {
+            atomicAdd(&a.counters[1], (unsigned long long)n_exec);
+            atomicAdd(&a.counters[2], (unsigned long long)n_skip);
+        }
+    }
+}
+
 // 16x16 blocks: thread (r, c) owns query row r of the block and output
 // columns c, c+16, ...; scores go through LDS.  The whole 16-row block is one
 // PV-skip group.
@@ -795,8 +1080,8 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
         const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
         if (a.bk == 64) {
             if (lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                if (a.D == 128) hipLaunchKernelGGL(k_flash_lam<128>, pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL(k_flash_lam<64>, pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             } else {
                 if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
                 else hipLaunchKernelGGL((k_flash_dma<64, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
