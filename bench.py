@@ -56,6 +56,17 @@ def flash_source_hash():
     return h.hexdigest()[:16]
 
 
+def attn_kernel_name(cfg):
+    """The attention kernel sa_sparse_attn_fwd launches for this configuration."""
+    if cfg.block_q == 16 and cfg.block_k == 16:
+        return "k_flash_small"
+    if cfg.lam is not None and cfg.block_k == 128:
+        return "k_flash_mfma"
+    if cfg.lam is not None:
+        return "k_flash_lam"
+    return "k_flash_dma"
+
+
 def executed_flops(cfg, rp, ci, skip, groups):
     """Executed QK and PV flops at real token counts, from the CSR and the PV-skip flags."""
     import numpy as np
@@ -288,7 +299,7 @@ def main():
         "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_flash_dma (+ k_attn_init), per sa_sparse_attn_fwd call",
+            "kernel": attn_kernel_name(cfg) + " (+ k_attn_init), per sa_sparse_attn_fwd call",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
