@@ -346,6 +346,14 @@ __device__ inline void dma16(int4v r, const uint16_t* dst, uint32_t off) {
         uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)dst)));
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
 }
+// LDS byte address of a __shared__ object
+__device__ inline uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+// as dma16, with the (wave-uniform) LDS byte address given as an integer
+__device__ inline void dma16_at(int4v r, uint32_t la, uint32_t off) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
+}
 // vmcnt(N): at most N of this wave's vector memory operations outstanding
 template <int N>
 __device__ inline void dma_wait() {
@@ -684,7 +692,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
     __shared__ __align__(16) uint16_t Ks[3][BK * D];
     __shared__ __align__(16) uint16_t Vs[BK * D];
-    __shared__ int need[2][4];  // need[t & 1][w]: wave w keeps the PV product of tile t
+    __shared__ uint32_t need[3];  // need[t % 3] bit w: wave w keeps the PV product of tile t
 
     const int G = a.B * a.Hq * a.n_qb;
     const int per = (G + 7) >> 3;
@@ -741,18 +749,20 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         const int rg = idx / SEG, seg = idx % SEG;
         return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
     };
+    const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DI * 1024);
+    const uint32_t vs_lds = lds_addr(&Vs[0]) + uint32_t(wave * DI * 1024);
     auto issue_k = [&](int kb0, int buf) {  // this wave's share of a K tile
 #pragma unroll
         for (int c = 0; c < DI; ++c) {
             const int idx = wave * DI + c;
-            dma16(rK, &Ks[buf][idx * 512], k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+            dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
         }
     };
     auto issue_v = [&](int kb0) {  // this wave's share of a V tile
 #pragma unroll
         for (int c = 0; c < DI; ++c) {
             const int idx = wave * DI + c;
-            dma16(rV, &Vs[idx * 512], v_lane + tile_base(kb0, idx));
+            dma16_at(rV, vs_lds + uint32_t(c * 1024), v_lane + tile_base(kb0, idx));
         }
     };
     // operand read offsets (elements): K for ks % 4, V for tt % 2
@@ -801,18 +811,23 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
         }
     };
-    auto any_need = [&](int par) { return (need[par][0] | need[par][1] | need[par][2] | need[par][3]) != 0; };
+    auto any_need = [&](int slot) { return __builtin_amdgcn_readfirstlane(need[slot]) != 0u; };
 
     if (nt > 0) issue_k(tile_key0(0), 0);
     if (nt > 1) issue_k(tile_key0(1), 1);
+    if (tid < 3) need[tid] = 0u;
     dma_wait<0>();
     __syncthreads();
-    int kbuf = 0;      // t % 3
+    int kbuf = 0;      // t % 3, also the need slot of tile t
     int prev_kb0 = -1;  // first key of tile t-1
     for (int t = 0; t < nt; ++t) {
         const int kb0 = tile_key0(t);
+        const int slot_prev = kbuf == 0 ? 2 : kbuf - 1;  // (t - 1) % 3
+        const int slot_next = kbuf == 2 ? 0 : kbuf + 1;  // (t + 1) % 3 == (t - 2) % 3
         // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
-        const bool vprev = t > 0 && any_need((t - 1) & 1);
+        const bool vprev = t > 0 && any_need(slot_prev);
+        // the mask of tile t-2 was read during iteration t-1: clear it for tile t+1
+        if (tid == 0) need[slot_next] = 0u;
         if (vprev) issue_v(prev_kb0);
         const bool kpre = t + 2 < nt;
         if (kpre) issue_k(tile_key0(t + 2), kbuf == 0 ? 2 : kbuf - 1);
@@ -898,7 +913,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             palpha = alpha;
         }
-        if (lane == 0) need[t & 1][wave] = my_need;
+        if (lane == 0 && my_need) atomicOr(&need[kbuf], 1u << wave);
         // K of tile t+1 has landed (that of t+2 may be in flight); V reads and
         // the need flags are complete
         if (kpre) dma_wait<DI>();
@@ -908,7 +923,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         prev_kb0 = kb0;
         kbuf = kbuf == 2 ? 0 : kbuf + 1;
     }
-    if (nt > 0 && any_need((nt - 1) & 1)) {
+    if (nt > 0 && any_need(kbuf == 0 ? 2 : kbuf - 1)) {
         issue_v(prev_kb0);
         dma_wait<0>();
         tile_barrier();
