@@ -38,6 +38,10 @@ SMALL = {
     "causal_s": rep(CONFIGS["causal_long"], Hq=4, Hkv=2, latent=(1, 1, 2000), window_tokens=512),
     "causal_s64": rep(CONFIGS["causal_long"], Hq=2, Hkv=1, latent=(1, 1, 777), window_tokens=300,
                       block_k=64, seed=51),
+    # PV skip on 128-key blocks, and on causal 64-key tiles (the diagonal masking path)
+    "image_s_lam": rep(CONFIGS["image"], Hq=3, Hkv=3, latent=(1, 20, 37), lam=-8.0, seed=61),
+    "causal_s64_lam": rep(CONFIGS["causal_long"], Hq=2, Hkv=1, latent=(1, 1, 777), window_tokens=300,
+                          block_k=64, lam=-8.0, seed=71),
 }
 
 
