@@ -1,7 +1,12 @@
 """Benchmark of the block-sparse attention forward path on one MI355X.
 
 A step is one pass of the whole path over one batch: reorder Q, K, V,
-predict the block mask, sparse attention, inverse reorder of the output.
+predict the block mask, sparse attention, inverse reorder of the output.  By
+default (bf16 inputs) the reorder is the gather form: the mask prediction and
+the attention read Q, K, V through the token permutation and the attention
+writes O back in the original order (two launches of work per step,
+bit-identical to the materialising form, which ``--form materialize`` times:
+three permute copies, prediction, attention, un-permute).
 Default workload: the long-video shape (B=1, 24 heads, latent [28,30,53] ->
 N=44520, d=128, Hilbert order, b_q=128 / b_k=64, tau=0.95, theta=0.6,
 lambda=-8) at sparsity 0.8.  Inputs are synthetic, seeded, and resident in
@@ -43,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
     ap.add_argument("--mode", default="path", choices=["path", "attn", "copy"])
+    ap.add_argument("--form", default="gather", choices=["gather", "materialize"],
+                    help="reorder inside the kernels' loads (bf16 inputs) or as separate copies")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
@@ -56,15 +63,16 @@ def flash_source_hash():
     return h.hexdigest()[:16]
 
 
-def attn_kernel_name(cfg):
-    """The attention kernel sa_sparse_attn_fwd launches for this configuration."""
+def attn_kernel_name(cfg, gather):
+    """The attention kernel the attention entry point launches for this configuration."""
     if cfg.block_q == 16 and cfg.block_k == 16:
         return "k_flash_small"
     if cfg.lam is not None and cfg.block_k == 128:
         return "k_flash_mfma"
+    g = "true" if gather else "false"
     if cfg.lam is not None:
-        return "k_flash_lam"
-    return "k_flash_dma"
+        return f"k_flash_lam<{cfg.D}, {g}>"
+    return f"k_flash_dma<{cfg.D}, {1 if cfg.block_k == 64 else 2}, {g}>"
 
 
 def executed_flops(cfg, rp, ci, skip, groups):
@@ -168,7 +176,8 @@ def main():
     if args.sparsity is not None:
         w = w.with_sparsity(args.sparsity)
     cfg = sa.config_from_workload(w)
-    path = sa.SparseAttentionPath(cfg)
+    gather = args.form == "gather" and w.dtype == "bf16"
+    path = sa.SparseAttentionPath(cfg, materialize=not gather)
     t_gen = time.perf_counter()
     q, k, v = generate(w)
     t_gen = time.perf_counter() - t_gen
@@ -181,17 +190,30 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     torch.cuda.synchronize()
 
+    # the step's stages; the gather form has no separate reorder copies
+    if gather:
+        stages = [("permute", lambda: None), ("predict", lambda: path.predict_gather(qd, kd)),
+                  ("attn", lambda: path.attend_gather(qd, kd, vd)), ("unpermute", lambda: None)]
+    else:
+        stages = [("permute", lambda: path.permute(qd, kd, vd)), ("predict", path.predict),
+                  ("attn", path.attend), ("unpermute", path.unpermute)]
+
+    def run_step():
+        for _, f in stages:
+            f()
+
     if args.mode == "attn":
-        path.run(qd, kd, vd)
+        run_step()
         for _ in range(max(1, args.steps)):
-            path.attend()
+            stages[2][1]()
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "attn", "launches": max(1, args.steps) + 1}))
+        print(json.dumps({"mode": "attn", "form": "gather" if gather else "materialize",
+                          "launches": max(1, args.steps) + 1}))
         return
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        path.run(qd, kd, vd)
+        run_step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -202,14 +224,9 @@ def main():
     start.record(stream)
     for s in range(K):
         e = ev[s]
-        e[0].record(stream)
-        path.permute(qd, kd, vd)
-        e[1].record(stream)
-        path.predict()
-        e[2].record(stream)
-        path.attend()
-        e[3].record(stream)
-        path.unpermute()
+        for j, (_, f) in enumerate(stages):
+            e[j].record(stream)
+            f()
         e[4].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -248,7 +265,7 @@ def main():
     n_qb, n_kb = cfg.n_qb, cfg.n_kb
     pred_bytes = (2 * (B * Hq * N * d + B * Hkv * N * d) + 4 * (B * Hq * n_qb + B * Hkv * n_kb) * d
                   + 4 * (B * Hq * n_qb + B * Hkv * n_kb) + 2 * B * Hq * n_qb * n_kb
-                  + 4 * (B * Hq * n_qb + 1) + 4 * nnz)
+                  + 4 * (B * Hq * n_qb + 1) + 4 * nnz + (4 * N if gather else 0))
     perm_bytes = (B * Hq * N * d + 2 * B * Hkv * N * d) * ((4 if w.dtype == "f32" else 2) + 2)
     unperm_bytes = 2 * 4 * B * Hq * N * d
 
@@ -257,7 +274,8 @@ def main():
         with open(TRAFFIC_FILE, encoding="utf8") as f:
             tr = json.load(f)
         if tr.get("source_sha") == flash_source_hash() and tr.get("workload") == args.workload \
-                and abs(tr.get("sparsity", -1) - (cfg.sparsity or 0)) < 1e-9:
+                and abs(tr.get("sparsity", -1) - (cfg.sparsity or 0)) < 1e-9 \
+                and tr.get("form", "materialize") == ("gather" if gather else "materialize"):
             traffic = tr["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -281,9 +299,11 @@ def main():
                          f"lambda{w.lam} sparsity{cfg.sparsity}"),
             "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "block_q": cfg.block_q, "block_k": cfg.block_k,
             "sparsity_target": cfg.sparsity,
+            "reorder": "gather (inside the kernels' loads)" if gather else "materialized copies",
         },
-        "ms": {"permute": round(stage[0], 4), "predict": round(stage[1], 4), "attn": round(attn_ms, 4),
-               "unpermute": round(stage[3], 4)},
+        "ms": ({"predict": round(stage[1], 4), "attn": round(attn_ms, 4)} if gather else
+               {"permute": round(stage[0], 4), "predict": round(stage[1], 4), "attn": round(attn_ms, 4),
+                "unpermute": round(stage[3], 4)}),
         "attn_executed_tflops": round(attn_tflops, 2),
         "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "dense_equiv_tflops_step": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
@@ -295,11 +315,12 @@ def main():
         "pv_group_blocks": {"executed": int(cnt[1]), "skipped": int(cnt[2])},
         "predict_gbs": round(pred_bytes / (stage[1] * 1e-3) / 1e9, 1),
         "predict_hbm_frac": round(pred_bytes / (stage[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "permute_gbs": round(perm_bytes / (stage[0] * 1e-3) / 1e9, 1),
-        "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1),
+        **({} if gather else {"permute_gbs": round(perm_bytes / (stage[0] * 1e-3) / 1e9, 1),
+                              "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1)}),
         "roofline": {
             "bound": "mfma",
-            "kernel": attn_kernel_name(cfg) + " (+ k_attn_init), per sa_sparse_attn_fwd call",
+            "kernel": attn_kernel_name(cfg, gather) + " (+ k_attn_init), per "
+                      + ("sa_sparse_attn_fwd_gather" if gather else "sa_sparse_attn_fwd") + " call",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -28,7 +28,7 @@ SA_MAX_KEY_BLOCKS = 2048
 
 EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermute",
            "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
-           "sa_sparse_attn_fwd")
+           "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather")
 
 
 class SaLayout(ctypes.Structure):
@@ -86,6 +86,14 @@ def lib() -> ctypes.CDLL:
     L.sa_sparse_attn_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(SaAttnParams),
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.sa_sparse_attn_fwd.restype = c_int
+    L.sa_predict_mask_gather.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(SaMaskParams), c_void_p, c_size_t,
+                                         c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p]
+    L.sa_predict_mask_gather.restype = c_int
+    L.sa_sparse_attn_fwd_gather.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            POINTER(SaAttnParams), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p]
+    L.sa_sparse_attn_fwd_gather.restype = c_int
     _lib = L
     return L
 
@@ -181,3 +189,22 @@ def sa_sparse_attn_fwd(q, k, v, o, p: SaAttnParams, row_ptr, col_idx, dev_status
                                     _ptr(col_idx), _ptr(pv_skip), _ptr(counters), _ptr(dev_status),
                                     _stream(stream))
     _check(code, "sa_sparse_attn_fwd")
+
+
+def sa_predict_mask_gather(q, k, perm, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mask_out=None,
+                           sim_q=None, sim_k=None, stream=None):
+    """sa_predict_mask on q[:, :, perm], k[:, :, perm] without materialising them (q, k bf16, original order)."""
+    code = lib().sa_predict_mask_gather(_ptr(q), _ptr(k), _ptr(perm), ctypes.byref(p), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _ptr(row_ptr), _ptr(col_idx),
+                                        col_idx.numel(), _ptr(mask_out), _ptr(sim_q), _ptr(sim_k),
+                                        _ptr(dev_status), _stream(stream))
+    _check(code, "sa_predict_mask_gather")
+
+
+def sa_sparse_attn_fwd_gather(q, k, v, perm, o, p: SaAttnParams, row_ptr, col_idx, dev_status, pv_skip=None,
+                              counters=None, stream=None):
+    """sa_sparse_attn_fwd on the reordered q, k, v, with o written back in the original order."""
+    code = lib().sa_sparse_attn_fwd_gather(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(o), ctypes.byref(p),
+                                           _ptr(row_ptr), _ptr(col_idx), _ptr(pv_skip), _ptr(counters),
+                                           _ptr(dev_status), _stream(stream))
+    _check(code, "sa_sparse_attn_fwd_gather")

@@ -76,6 +76,8 @@ int validate_attn(const sa_attn_params* p) {
     if (p->col_cap < 0) return SA_ERR_INVALID_ARGUMENT;
     if (!std::isfinite(p->scale) || p->scale < 0.0f) return SA_ERR_INVALID_ARGUMENT;
     if (p->D != p->Dv || !head_dim_ok(p->D)) return SA_ERR_UNSUPPORTED;
+    // one head of k or v is addressed with 32-bit byte offsets below 2^31
+    if (p->N * p->D * 2 >= (int64_t(1) << 31)) return SA_ERR_UNSUPPORTED;
     const bool pair_ok = (p->block_q == 16 && p->block_k == 16) ||
                          (p->block_q == 128 && (p->block_k == 64 || p->block_k == 128));
     if (!pair_ok) return SA_ERR_UNSUPPORTED;
@@ -133,10 +135,11 @@ extern "C" int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off
     return SA_OK;
 }
 
-extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* p,
-                               void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
-                               int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
-                               int32_t* dev_status, void* stream) {
+namespace {
+
+int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, const sa_mask_params* p,
+                 void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                 uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status, void* stream) {
     PredictShape s;
     const int st = predict_shape(p, &s);
     if (st != SA_OK) return st;
@@ -155,7 +158,7 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
     uint8_t* mask = reinterpret_cast<uint8_t*>(base + s.off[4]);
     int32_t* counts = reinterpret_cast<int32_t*>(base + s.off[5]);
 
-    hipError_t e = launch_block_stats(q, k, s, qbar, kbar, simq, simk, dev_status, hs);
+    hipError_t e = launch_block_stats(q, k, perm, s, qbar, kbar, simq, simk, dev_status, hs);
     if (e != hipSuccess) return SA_ERR_HIP;
 
     TopCdfArgs a;
@@ -192,10 +195,9 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
     return SA_OK;
 }
 
-extern "C" int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
-                                  const sa_attn_params* p, const int32_t* row_ptr,
-                                  const int32_t* col_idx, uint8_t* pv_skip, int64_t* counters,
-                                  int32_t* dev_status, void* stream) {
+int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* perm, float* o,
+                    const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
+                    int64_t* counters, int32_t* dev_status, void* stream) {
     const int st = validate_attn(p);
     if (st != SA_OK) return st;
     if (!q || !k || !v || !o || !row_ptr || !col_idx || !dev_status) return SA_ERR_INVALID_ARGUMENT;
@@ -204,7 +206,7 @@ extern "C" int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const ui
         return SA_ERR_INVALID_ARGUMENT;
     FlashArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
-    a.row_ptr = row_ptr; a.col_idx = col_idx; a.pv_skip = pv_skip;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.perm = perm; a.pv_skip = pv_skip;
     a.counters = reinterpret_cast<unsigned long long*>(counters);
     a.dev_status = dev_status;
     a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.D = p->D; a.N = p->N;
@@ -217,4 +219,38 @@ extern "C" int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const ui
     a.scale = p->scale > 0.0f ? p->scale : float(1.0 / std::sqrt(double(p->D)));
     const hipError_t e = launch_flash(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* p,
+                               void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
+                               int32_t* dev_status, void* stream) {
+    return predict_mask(q, k, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+                        dev_status, stream);
+}
+
+extern "C" int sa_predict_mask_gather(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                                      const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr,
+                                      int32_t* col_idx, int64_t col_cap, uint8_t* mask_out, float* sim_q,
+                                      float* sim_k, int32_t* dev_status, void* stream) {
+    if (!perm_dev) return SA_ERR_INVALID_ARGUMENT;
+    return predict_mask(q, k, perm_dev, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+                        dev_status, stream);
+}
+
+extern "C" int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
+                                  const sa_attn_params* p, const int32_t* row_ptr,
+                                  const int32_t* col_idx, uint8_t* pv_skip, int64_t* counters,
+                                  int32_t* dev_status, void* stream) {
+    return sparse_attn_fwd(q, k, v, nullptr, o, p, row_ptr, col_idx, pv_skip, counters, dev_status, stream);
+}
+
+extern "C" int sa_sparse_attn_fwd_gather(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* perm_dev, float* o, const sa_attn_params* p,
+                                         const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
+                                         int64_t* counters, int32_t* dev_status, void* stream) {
+    if (!perm_dev) return SA_ERR_INVALID_ARGUMENT;
+    return sparse_attn_fwd(q, k, v, perm_dev, o, p, row_ptr, col_idx, pv_skip, counters, dev_status, stream);
 }

@@ -3,8 +3,11 @@
 // blocks outside the mask skip both QK^T and PV; section 2.3: PV skip when
 // the running-max gap of a row group is below lambda).
 //
-// k_flash_dma<D, SUB, LAM>: the production kernel for 64-key tiles (and for
-// 128-key blocks without PV skip, as two 64-key steps); see its comment.
+// k_flash_dma<D, SUB, GATHER>, k_flash_lam<D, GATHER>: the production kernels
+// for 64-key tiles without and with PV skip (k_flash_dma also runs 128-key
+// blocks without PV skip, as two 64-key tiles); see their comment.  GATHER
+// reads q, k, v through the token permutation and stores O back in the
+// original order.
 //
 // k_flash_mfma<D, BK>: one workgroup of 4 wavefronts per 128-row query block;
 // wavefront w owns query rows 32w..32w+31 and is the PV-skip group.  Scores
@@ -18,6 +21,9 @@
 // contiguous LDS reads.
 //
 // k_flash_small<D>: the 16x16-block case (tiny workloads), plain fp32 ALU.
+//
+// The last two map rows through the permutation (when given) one load at a
+// time.
 #include <cmath>
 #include <type_traits>
 
@@ -62,6 +68,15 @@ __global__ void k_attn_init(int32_t* status, unsigned long long* counters) {
     if (counters) counters[0] = counters[1] = counters[2] = 0ull;
 }
 
+// Source row of position i of the reordered sequence: perm[i], or i without a
+// permutation.  An entry outside 0..N-1 (perm is then no permutation) reads
+// row 0 instead of leaving the tensor.
+__device__ inline int64_t src_row(const int32_t* perm, int64_t i, int64_t N) {
+    if (!perm) return i;
+    const int32_t r = perm[i];
+    return (r >= 0 && r < N) ? r : 0;
+}
+
 template <int D, int BK>
 __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     constexpr int BQ = 128;
@@ -96,11 +111,12 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     const bool row_valid = qrow < N;
     const bool wave_rows = wrow0 < N;
 
+    const int64_t qsrc = row_valid ? src_row(a.perm, qrow, N) : 0;
     bf16x8_t qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4*>(Qh + qrow * D + ks * 16 + half * 8);
+        if (row_valid) u = *reinterpret_cast<const uint4*>(Qh + qsrc * D + ks * 16 + half * 8);
         qf[ks] = as_bf16x8(u);
     }
 
@@ -136,7 +152,7 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
         for (int c = tid; c < BK * KCH; c += 256) {
             const int rr = c / KCH, cc = c % KCH;
             uint4 u = make_uint4(0, 0, 0, 0);
-            if (kb0 + rr < N) u = *reinterpret_cast<const uint4*>(Kh + (kb0 + rr) * D + cc * 8);
+            if (kb0 + rr < N) u = *reinterpret_cast<const uint4*>(Kh + src_row(a.perm, kb0 + rr, N) * D + cc * 8);
             *reinterpret_cast<uint4*>(Ks + rr * KSTR + cc * 8) = u;
         }
         // ---- V tile, transposed through 4x4 register blocks
@@ -148,7 +164,8 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int64_t key = kb0 + kb4 * 4 + rr;
-                rv[rr] = key < N ? *reinterpret_cast<const uint2*>(Vh + key * D + db4 * 4) : make_uint2(0, 0);
+                rv[rr] = key < N ? *reinterpret_cast<const uint2*>(Vh + src_row(a.perm, key, N) * D + db4 * 4)
+                                 : make_uint2(0, 0);
             }
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     if (row_valid) {
         const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
         if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
-        float* orow = Oh + qrow * D;
+        float* orow = Oh + qsrc * D;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -295,24 +312,26 @@ __device__ inline float max_lanes32(float v) {
     return fmaxf(r0, r1);
 }
 
-// DMA variant (the production path for 64-key tiles).  K and V tiles go
+// LDS-DMA kernels (the production path for 64-key tiles).  K and V tiles go
 // straight from HBM/L2 into LDS with buffer_load ... lds (16 bytes per lane,
-// rows past the sequence end read as zero).  Each 1 KB DMA instruction moves
-// 8 rows x 128 bytes (whole cache lines); in LDS the 16-byte chunks of row r
-// are XOR-permuted (K: by (r>>1)&7, V: by r&7) so that the MFMA operand reads
-// are bank-conflict free: the K operand (ds_read_b128, key row 32mt+(l&31),
+// out-of-range rows read as zero).  Each 1 KB DMA instruction moves 8 rows x
+// 128 bytes (whole cache lines); in LDS the 16-byte chunks of row r are
+// XOR-permuted (K: by (r>>1)&7, V: by r&7) so that the MFMA operand reads are
+// bank-conflict free: the K operand (ds_read_b128, key row 32mt+(l&31),
 // head-dim chunk 2ks+(l>>5)) and the transposed V operand (ds_read_b64_tr_b16:
 // in each 16-lane group lane i slot j receives element i&3 of the 8 bytes
 // lane 4j+i/4 read, so lane l reads
 // V[16ps + 8ab + 4(l>>5) + ((l&15)>>2)][32tt + 16((l>>4)&1) + 4(l&3) .. +3]).
-// All read addresses are one of a few per-lane offsets plus an immediate.
+// All operand read addresses are one of a few per-lane offsets plus an
+// immediate.
 //
-// With PV skip on (LAM) most tiles never need V: K runs two tiles ahead in
-// three LDS buffers, and V is fetched only by a wavefront that runs the PV
-// product of the tile, into a single buffer (all waves sit in the same tile
-// between barriers).  Without PV skip, K and V run one tile ahead in two
-// buffers each.  The skip test of a 32-row group is one ballot: skip when no
-// valid row's block maximum comes within lambda of its new running maximum.
+// GATHER: q, k and v stay in the caller's token order and position i of the
+// reordered sequence is row perm[i] (the reorder is an index map, not a
+// copy).  Each tile's 64 entries of perm are DMA'd into a small LDS ring
+// several tiles ahead; every lane reads the source rows of its DMA lines from
+// there one iteration before it issues them, and O rows are stored back at
+// their original positions.  The arithmetic is unchanged, so the output equals
+// that of the same kernel on reordered copies bit for bit.
 //
 // The exponentials are taken against the running maximum itself, so the
 // largest probability of the row is exactly 1 (exact in bf16 for the PV
@@ -329,30 +348,40 @@ __device__ inline void tile_barrier() { asm volatile("s_barrier" ::: "memory"); 
 // this wave's LDS reads and writes are complete
 __device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Buffer resource (descriptor words) over one head's rows, for the DMA below.
+// Buffer resource (descriptor words) over `bytes` bytes at `base`, for the DMA
+// below; offsets at or past `bytes` read as zero.
 typedef int int4v __attribute__((ext_vector_type(4)));
 __device__ inline int4v head_desc(const void* base, uint32_t bytes) {
     const uint64_t p = reinterpret_cast<uint64_t>(base);
     return int4v{int(uint32_t(p)), int(uint32_t(p >> 32) & 0xffff), int(bytes), 0x00020000};
 }
-
-// 16 bytes per lane from buffer `r` at byte offset `off` into LDS at dst + 16*lane.
-// Issued as assembly so the compiler does not track it: it would otherwise
-// wait for every outstanding LDS DMA before any LDS read.  The kernels wait
-// explicitly (dma_wait) before reading a DMA'd buffer.
-__device__ inline void dma16(int4v r, const uint16_t* dst, uint32_t off) {
-    // the LDS address is wave-uniform; M0 is handed to the compiler as an operand
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)dst)));
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
-}
 // LDS byte address of a __shared__ object
 __device__ inline uint32_t lds_addr(const void* p) {
     return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
-// as dma16, with the (wave-uniform) LDS byte address given as an integer
+// 16 (dma16_at) or 4 (dma4_at) bytes per lane from buffer `r` at byte offset
+// `off` into LDS at la + lane * size; `la` is wave-uniform.  Issued as assembly
+// so the compiler does not track it (it would otherwise wait for every
+// outstanding LDS DMA before any LDS read); the kernels wait explicitly
+// (dma_wait) before the barrier that publishes a DMA'd buffer.  M0 is handed
+// to the compiler as an operand.  The compiler does not pad hazards into
+// inline assembly, so the leading s_nop supplies the five wait states a vector
+// memory instruction needs after a VALU write of an SGPR it reads (the
+// descriptor can be restored from a spill with v_readlane right before), which
+// also covers the one after the write of M0.
 __device__ inline void dma16_at(int4v r, uint32_t la, uint32_t off) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
+}
+__device__ inline void dma4_at(int4v r, uint32_t la, uint32_t off) {
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" :: "v"(off), "s"(r), "{m0}"(la) : "memory");
+}
+// Marks the Q fragments as consumed here, so the compiler waits for their
+// loads once, before the tile loop, instead of inside it (where its count
+// would also wait for the untracked tile DMAs in flight).
+template <int KS>
+__device__ inline void q_ready(const bf16x8_t (&qf)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qf[ks]));
 }
 // vmcnt(N): at most N of this wave's vector memory operations outstanding
 template <int N>
@@ -364,7 +393,36 @@ __device__ inline void dma_wait() {
     else static_assert(N == 0 || N == 2 || N == 4, "add the count");
 }
 
-template <int D, int SUB, bool LAM>
+constexpr int kRing = 8;  // LDS ring of per-tile source rows (GATHER)
+
+// Per-lane part of the tile DMA.  Instruction c of wave w moves rows
+// 8*rg .. 8*rg+7 (rg = 2w + c/SEG) of 128-byte segment c % SEG of a 64-row
+// tile; lane L carries row 8*rg + L/8 into LDS position L%8 of that line, so
+// it reads source chunk (L%8) ^ swizzle(row).  A lane thus moves rows
+// r0 = 16w + L/8 and r0 + 8 of every tile.
+template <int D>
+struct TileLane {
+    static constexpr int SEG = D / 64;
+    int r0;
+    uint32_t kch[2][SEG];  // K: chunk offset of row r0 + 8x plus segment offset
+    uint32_t vch[SEG];     // V: the same (the V swizzle is equal for both rows)
+    __device__ TileLane(int wave, int lane) {
+        const int dq = lane >> 3, dp = lane & 7;
+        r0 = 16 * wave + dq;
+#pragma unroll
+        for (int s = 0; s < SEG; ++s) {
+            kch[0][s] = uint32_t((dp ^ ((dq >> 1) & 7)) * 16 + s * 128);
+            kch[1][s] = uint32_t((dp ^ ((4 + (dq >> 1)) & 7)) * 16 + s * 128);
+            vch[s] = uint32_t((dp ^ dq) * 16 + s * 128);
+        }
+    }
+    __device__ uint32_t k_off(const uint32_t (&rb)[2], int c) const { return rb[c / SEG] + kch[c / SEG][c % SEG]; }
+    __device__ uint32_t v_off(const uint32_t (&rb)[2], int c) const { return rb[c / SEG] + vch[c % SEG]; }
+};
+
+// lambda off: every kept tile runs its PV product.  K and V run one tile
+// ahead in two LDS buffers each.  128-key blocks run as two 64-key tiles.
+template <int D, int SUB, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                  uint8_t* __restrict__ pv_skip) {
@@ -374,18 +432,16 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int KS = D / 16;               // MFMA k-steps over the head dim
     constexpr int SEG = D / 64;              // 128-byte segments per row
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
-    // One array per buffer, selected at compile time: the compiler can then
-    // prove that a DMA into one buffer does not alias operand reads from
-    // another and does not wait for it.
+    // One array per buffer, selected at compile time, so that operand reads
+    // use constant LDS addresses.
     __shared__ __align__(16) uint16_t Ks0[BK * D];
     __shared__ __align__(16) uint16_t Ks1[BK * D];
-    __shared__ __align__(16) uint16_t Ks2[LAM ? BK * D : 8];
     __shared__ __align__(16) uint16_t Vs0[BK * D];
-    __shared__ __align__(16) uint16_t Vs1[LAM ? 8 : BK * D];
+    __shared__ __align__(16) uint16_t Vs1[BK * D];
+    __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
     auto kbuf_of = [&](auto I) -> uint16_t* {
         if constexpr (decltype(I)::value == 0) return Ks0;
-        else if constexpr (decltype(I)::value == 1) return Ks1;
-        else return Ks2;
+        else return Ks1;
     };
     auto vbuf_of = [&](auto I) -> uint16_t* {
         if constexpr (decltype(I)::value == 0) return Vs0;
@@ -415,13 +471,15 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int qrow = wrow0 + l32;
     const bool row_valid = qrow < N;
     const bool wave_rows = wrow0 < N;
+    int qsrc = qrow;  // source row of this lane's query; past the end it reads zeros
+    if constexpr (GATHER) qsrc = row_valid ? a.perm[qrow] : N;
 
     bf16x8_t qf[KS];
     {
         const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qrow * D + ks * 16 + half * 8) * 2u));
+            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qsrc * D + ks * 16 + half * 8) * 2u));
     }
 
     const int e0 = row_ptr[row];
@@ -437,34 +495,41 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         if (j < 0 || j >= a.n_kb) return -1;
         return j * (BK * SUB) + (t % SUB) * BK;
     };
-    // DMA: instruction idx covers rows 8*rg .. 8*rg+7 (rg = idx / SEG) of segment idx % SEG;
-    // lane L moves row 8*rg + L/8, LDS position L%8, i.e. source chunk (L%8) ^ swizzle(row)
-    const int dq = lane >> 3, dp = lane & 7;
-    const uint32_t k_lane[2] = {uint32_t(dq * D * 2 + ((dp ^ ((dq >> 1) & 7)) * 16)),
-                                uint32_t(dq * D * 2 + ((dp ^ ((4 + (dq >> 1)) & 7)) * 16))};
-    const uint32_t v_lane = uint32_t(dq * D * 2 + ((dp ^ dq) * 16));
-    auto tile_base = [&](int kb0, int idx) -> uint32_t {  // uniform part of the source offset
-        const int rg = idx / SEG, seg = idx % SEG;
-        return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
-    };
-    auto issue_k = [&](int kb0, uint16_t* dst) {
-#pragma unroll
-        for (int c = 0; c < DI; ++c) {
-            const int idx = wave * DI + c;
-            dma16(rK, dst + idx * 512, k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+    const TileLane<D> tl(wave, lane);
+    const int4v rP = head_desc(a.perm, uint32_t(N) * 4u);
+    const uint32_t pr_lds = lds_addr(&prow[0][0]);
+    // wave 0 fetches the source rows of tile t into ring slot t % kRing
+    auto issue_perm = [&](int t) {
+        if constexpr (GATHER) {
+            const int key0 = tile_key0(t);
+            if (wave == 0 && key0 >= 0)
+                dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4), uint32_t(key0 + lane) * 4u);
         }
     };
-    auto issue_v = [&](int kb0, uint16_t* dst) {  // this wave's share of the V tile
+    // byte offsets of this lane's two source rows of tile t; an invalid tile
+    // or a row past the end gets an offset beyond the buffer (reads zeros)
+    auto tile_rows = [&](int t, uint32_t (&rb)[2]) {
+        const int key0 = tile_key0(t);
+        if constexpr (GATHER) {
 #pragma unroll
-        for (int c = 0; c < DI; ++c) {
-            const int idx = wave * DI + c;
-            dma16(rV, dst + idx * 512, v_lane + tile_base(kb0, idx));
+            for (int x = 0; x < 2; ++x) {
+                const int r = tl.r0 + 8 * x;
+                const bool ok = key0 >= 0 && key0 + r < N;
+                rb[x] = ok ? uint32_t(prow[t % kRing][r]) * uint32_t(D * 2) : 0x80000000u;
+            }
+        } else {
+            const uint32_t base = key0 < 0 ? 0x80000000u : uint32_t(key0) * uint32_t(D * 2);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
         }
     };
-    auto issue_v_all = [&](int kb0) {  // the whole V tile by this wave alone
-#pragma unroll 1
-        for (int idx = 0; idx < 4 * DI; ++idx)
-            dma16(rV, Vs0 + idx * 512, v_lane + tile_base(kb0, idx));
+    auto issue_kv = [&](const uint32_t (&rb)[2], auto KN) {
+        const uint32_t kl = lds_addr(kbuf_of(KN)) + uint32_t(wave * DI * 1024);
+        const uint32_t vl = lds_addr(vbuf_of(KN)) + uint32_t(wave * DI * 1024);
+#pragma unroll
+        for (int c = 0; c < DI; ++c) dma16_at(rK, kl + uint32_t(c * 1024), tl.k_off(rb, c));
+#pragma unroll
+        for (int c = 0; c < DI; ++c) dma16_at(rV, vl + uint32_t(c * 1024), tl.v_off(rb, c));
     };
     // operand read offsets (elements): K for ks % 4, V for tt % 2
     int k_off[4], v_off[2];
@@ -486,28 +551,20 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     float m_run = -INFINITY;  // running max in raw score units (q.k)
     float l_part = 0.f;
     const float c2 = a.scale * kLog2e;
-    const float lam_raw = a.lambda / a.scale;
-    int n_exec = 0, n_skip = 0;
+    int n_exec = 0;
     bool bad_col = false;
+    uint32_t nr[2];  // source rows of the next tile to fetch
 
-    // tile t: K in buffer KC; DMA target of the next K (t+2 with PV skip, t+1
-    // without) is buffer KN; without PV skip V of tile t is in buffer KC too
+    // tile t: K and V in buffer KC; tile t+1 goes to buffer KN
     auto step = [&](int t, auto KC, auto KN) {
         const int kb0 = tile_key0(t);
-        if constexpr (LAM) {
-            if (t + 2 < nt) issue_k(tile_key0(t + 2), kbuf_of(KN));
-        } else {
-            if (t + 1 < nt) {
-                const int kn = tile_key0(t + 1);
-                issue_k(kn, kbuf_of(KN));
-                issue_v(kn, vbuf_of(KN));
-            }
-        }
+        if (GATHER && t + 3 < nt) issue_perm(t + 3);
+        if (t + 1 < nt) issue_kv(nr, KN);
+        // ring slot t+2 was filled during iteration t-1
+        if (t + 2 < nt) tile_rows(t + 2, nr);
         if (kb0 < 0) {
             bad_col = true;
-        } else if (!wave_rows) {
-            if (LAM && pv_skip && lane == 0 && t % SUB == 0) pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = 0;
-        } else {
+        } else if (wave_rows) {
             const uint16_t* K = kbuf_of(KC);
             floatx16 s0, s1;
 #pragma unroll
@@ -539,15 +596,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             float lo, hi;
             swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
-            const float smax = max2f(lo, hi);
-            const float m_new = max2f(m_run, smax);
-            bool skip = false;
-            if constexpr (LAM) {
-                // NaN (no key yet) and -inf gaps never reach lambda
-                skip = __builtin_amdgcn_ballot_w64(row_valid && smax - m_new >= lam_raw) == 0ull;
-            }
-            // a skipped tile never raises a valid row's maximum, so O and l
-            // are rescaled here only on tiles that also run their PV product
+            const float m_new = max2f(m_run, max2f(lo, hi));
             if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
                 const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);  // 0 when m_run = -inf
                 l_part *= alpha;
@@ -567,88 +616,65 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
             for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
             l_part += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-            if (LAM && pv_skip && lane == 0 && t % SUB == 0)
-                pv_skip[int64_t(e0 + t / SUB) * 4 + wave] = skip ? 1 : 0;
-            if (skip) {
-                ++n_skip;
-            } else {
-                ++n_exec;
-                const uint16_t* Vt = vbuf_of(KC);
-                if constexpr (LAM) {
-                    // fetch the tile now (other waves may do the same concurrently;
-                    // they write identical bytes)
-                    issue_v_all(kb0);
-                    dma_wait<0>();
-                    Vt = Vs0;
-                }
-                bf16x8_t pb[4];
+            ++n_exec;
+            bf16x8_t pb[4];
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    pb[0][x] = (__bf16)s0[x];
-                    pb[1][x] = (__bf16)s0[8 + x];
-                    pb[2][x] = (__bf16)s1[x];
-                    pb[3][x] = (__bf16)s1[8 + x];
-                }
+            for (int x = 0; x < 8; ++x) {
+                pb[0][x] = (__bf16)s0[x];
+                pb[1][x] = (__bf16)s0[8 + x];
+                pb[2][x] = (__bf16)s1[x];
+                pb[3][x] = (__bf16)s1[8 + x];
+            }
+            const uint16_t* Vt = vbuf_of(KC);
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-                    for (int ps4 = 0; ps4 < 4; ++ps4) {
-                        const uint16_t* pa = Vt + v_off[tt & 1] + ((2 * ps4) * SEG + (tt >> 1)) * 512;
-                        const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
-                        const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(pa + SEG * 512));
-                        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps4], oacc[tt], 0, 0, 0);
-                    }
+                for (int ps4 = 0; ps4 < 4; ++ps4) {
+                    const uint16_t* pa = Vt + v_off[tt & 1] + ((2 * ps4) * SEG + (tt >> 1)) * 512;
+                    const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)pa);
+                    const short4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(pa + SEG * 512));
+                    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps4], oacc[tt], 0, 0, 0);
                 }
             }
         }
-        // the K tile of t+1 (and its V without PV skip) has landed; with PV skip
-        // the K tile of t+2 may still be in flight.  Operand reads of tile t
-        // are complete (consumed by the MFMAs).
-        if constexpr (LAM) {
-            if (t + 2 < nt) dma_wait<DI>();
-            else dma_wait<0>();
-        } else {
-            dma_wait<0>();
-        }
-        tile_barrier();  // ... and everyone's; the buffers of tile t are free again
+        // the tiles of t+1 (and the source rows of t+3) have landed; the
+        // operand reads of tile t are complete (consumed by the MFMAs)
+        dma_wait<0>();
+        tile_barrier();  // ... everyone's; the buffers of tile t are free again
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
+    if constexpr (GATHER) {
+        for (int t = 0; t < 3 && t < nt; ++t) issue_perm(t);
+        dma_wait<0>();
+        tile_barrier();
+    }
     if (nt > 0) {
-        issue_k(tile_key0(0), Ks0);
-        if constexpr (!LAM) issue_v(tile_key0(0), Vs0);
+        uint32_t rb[2];
+        tile_rows(0, rb);
+        issue_kv(rb, I0{});
     }
-    if constexpr (LAM) {
-        if (nt > 1) issue_k(tile_key0(1), Ks1);
-    }
+    if (nt > 1) tile_rows(1, nr);
     dma_wait<0>();
     __syncthreads();
-    if constexpr (LAM) {
-        for (int t = 0; t < nt; t += 3) {
-            step(t, I0{}, I2{});
-            if (t + 1 < nt) step(t + 1, I1{}, I0{});
-            if (t + 2 < nt) step(t + 2, I2{}, I1{});
-        }
-    } else {
-        for (int t = 0; t < nt; t += 2) {
-            step(t, I0{}, I1{});
-            if (t + 1 < nt) step(t + 1, I1{}, I0{});
-        }
+    q_ready(qf);
+    for (int t = 0; t < nt; t += 2) {
+        step(t, I0{}, I1{});
+        if (t + 1 < nt) step(t + 1, I1{}, I0{});
     }
-    if (!LAM && pv_skip && lane == 0)
+    if (pv_skip && lane == 0)
         for (int e = e0; e < e1; ++e) pv_skip[int64_t(e) * 4 + wave] = 0;
     if (bad_col && tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
 
     float l_lo, l_hi;
     swap32(l_part, l_lo, l_hi);
     const float l_tot = l_lo + l_hi;
-    if (row_valid) {
+    if (row_valid && uint32_t(qsrc) < uint32_t(N)) {  // entries of perm outside 0..N-1 store nothing
         const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
         if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
-        float* orow = a.o + int64_t(bh) * N * D + int64_t(qrow) * D;
+        float* orow = a.o + (int64_t(bh) * N + qsrc) * D;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -663,10 +689,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     }
     if (a.counters) {
         if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)(e1 > e0 ? e1 - e0 : 0));
-        if (lane == 0 && wave_rows) {
-            atomicAdd(&a.counters[1], (unsigned long long)((n_exec + SUB - 1) / SUB));
-            atomicAdd(&a.counters[2], (unsigned long long)(n_skip / SUB));
-        }
+        if (lane == 0 && wave_rows) atomicAdd(&a.counters[1], (unsigned long long)((n_exec + SUB - 1) / SUB));
     }
 }
 
@@ -679,8 +702,10 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 // O <- alpha O + P V for tile t-1.  O therefore lags one tile behind m and l;
 // a skipped tile never raises a valid row's maximum (its alpha is 1), so only
 // kept tiles carry a pending rescale.  K runs two tiles ahead in three
-// buffers; V needs one buffer.
-template <int D>
+// buffers; V needs one buffer.  The skip test of a 32-row group is one
+// ballot: skip when no valid row's block maximum comes within lambda of its
+// new running maximum.
+template <int D, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                  uint8_t* __restrict__ pv_skip) {
@@ -692,6 +717,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
     __shared__ __align__(16) uint16_t Ks[3][BK * D];
     __shared__ __align__(16) uint16_t Vs[BK * D];
+    __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
     __shared__ uint32_t need[3];  // need[t % 3] bit w: wave w keeps the PV product of tile t
 
     const int G = a.B * a.Hq * a.n_qb;
@@ -717,13 +743,15 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int qrow = wrow0 + l32;
     const bool row_valid = qrow < N;
     const bool wave_rows = wrow0 < N;
+    int qsrc = qrow;  // source row of this lane's query; past the end it reads zeros
+    if constexpr (GATHER) qsrc = row_valid ? a.perm[qrow] : N;
 
     bf16x8_t qf[KS];
     {
         const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qrow * D + ks * 16 + half * 8) * 2u));
+            qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qsrc * D + ks * 16 + half * 8) * 2u));
     }
 
     const int e0 = row_ptr[row];
@@ -739,31 +767,44 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         if (j < 0 || j >= a.n_kb) return -1;
         return j * BK;
     };
-    // DMA: instruction idx covers rows 8*rg .. 8*rg+7 (rg = idx / SEG) of segment idx % SEG;
-    // lane L moves row 8*rg + L/8, LDS position L%8, i.e. source chunk (L%8) ^ swizzle(row)
-    const int dq = lane >> 3, dp = lane & 7;
-    const uint32_t k_lane[2] = {uint32_t(dq * D * 2 + ((dp ^ ((dq >> 1) & 7)) * 16)),
-                                uint32_t(dq * D * 2 + ((dp ^ ((4 + (dq >> 1)) & 7)) * 16))};
-    const uint32_t v_lane = uint32_t(dq * D * 2 + ((dp ^ dq) * 16));
-    auto tile_base = [&](int kb0, int idx) -> uint32_t {  // uniform part of the source offset
-        const int rg = idx / SEG, seg = idx % SEG;
-        return kb0 < 0 ? 0x80000000u : uint32_t(kb0 + 8 * rg) * (D * 2u) + uint32_t(seg * 128);
-    };
+    const TileLane<D> tl(wave, lane);
+    const int4v rP = head_desc(a.perm, uint32_t(N) * 4u);
+    const uint32_t pr_lds = lds_addr(&prow[0][0]);
     const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DI * 1024);
     const uint32_t vs_lds = lds_addr(&Vs[0]) + uint32_t(wave * DI * 1024);
-    auto issue_k = [&](int kb0, int buf) {  // this wave's share of a K tile
-#pragma unroll
-        for (int c = 0; c < DI; ++c) {
-            const int idx = wave * DI + c;
-            dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), k_lane[(c / SEG) & 1] + tile_base(kb0, idx));
+    // wave 0 fetches the source rows of tile t into ring slot t % kRing
+    auto issue_perm = [&](int t) {
+        if constexpr (GATHER) {
+            const int key0 = tile_key0(t);
+            if (wave == 0 && key0 >= 0)
+                dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4), uint32_t(key0 + lane) * 4u);
         }
     };
-    auto issue_v = [&](int kb0) {  // this wave's share of a V tile
+    // byte offsets of this lane's two source rows of the tile starting at
+    // key0 (tile t); an invalid tile or a row past the end gets an offset
+    // beyond the buffer (reads zeros)
+    auto tile_rows = [&](int key0, int t, uint32_t (&rb)[2]) {
+        if constexpr (GATHER) {
 #pragma unroll
-        for (int c = 0; c < DI; ++c) {
-            const int idx = wave * DI + c;
-            dma16_at(rV, vs_lds + uint32_t(c * 1024), v_lane + tile_base(kb0, idx));
+            for (int x = 0; x < 2; ++x) {
+                const int r = tl.r0 + 8 * x;
+                const bool ok = key0 >= 0 && key0 + r < N;
+                rb[x] = ok ? uint32_t(prow[t % kRing][r]) * uint32_t(D * 2) : 0x80000000u;
+            }
+        } else {
+            const uint32_t base = key0 < 0 ? 0x80000000u : uint32_t(key0) * uint32_t(D * 2);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
         }
+    };
+    auto issue_k = [&](const uint32_t (&rb)[2], int buf) {  // this wave's share of a K tile
+#pragma unroll
+        for (int c = 0; c < DI; ++c)
+            dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), tl.k_off(rb, c));
+    };
+    auto issue_v = [&](const uint32_t (&rb)[2]) {  // this wave's share of a V tile
+#pragma unroll
+        for (int c = 0; c < DI; ++c) dma16_at(rV, vs_lds + uint32_t(c * 1024), tl.v_off(rb, c));
     };
     // operand read offsets (elements): K for ks % 4, V for tt % 2
     int k_off[4], v_off[2];
@@ -813,13 +854,28 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     };
     auto any_need = [&](int slot) { return __builtin_amdgcn_readfirstlane(need[slot]) != 0u; };
 
-    if (nt > 0) issue_k(tile_key0(0), 0);
-    if (nt > 1) issue_k(tile_key0(1), 1);
+    // kr: source rows of the next K tile to fetch (t+2 during iteration t);
+    // vr: those of tile t-1, whose V may be fetched during iteration t
+    uint32_t kr[2], vr[2];
+    if constexpr (GATHER) {
+        for (int t = 0; t < 4 && t < nt; ++t) issue_perm(t);
+        dma_wait<0>();
+        tile_barrier();
+    }
+    if (nt > 0) {
+        tile_rows(tile_key0(0), 0, kr);
+        issue_k(kr, 0);
+    }
+    if (nt > 1) {
+        tile_rows(tile_key0(1), 1, kr);
+        issue_k(kr, 1);
+    }
+    if (nt > 2) tile_rows(tile_key0(2), 2, kr);
     if (tid < 3) need[tid] = 0u;
     dma_wait<0>();
     __syncthreads();
-    int kbuf = 0;      // t % 3, also the need slot of tile t
-    int prev_kb0 = -1;  // first key of tile t-1
+    q_ready(qf);
+    int kbuf = 0;  // t % 3, also the need slot of tile t
     for (int t = 0; t < nt; ++t) {
         const int kb0 = tile_key0(t);
         const int slot_prev = kbuf == 0 ? 2 : kbuf - 1;  // (t - 1) % 3
@@ -828,9 +884,14 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         const bool vprev = t > 0 && any_need(slot_prev);
         // the mask of tile t-2 was read during iteration t-1: clear it for tile t+1
         if (tid == 0) need[slot_next] = 0u;
-        if (vprev) issue_v(prev_kb0);
+        if (GATHER && t + 4 < nt) issue_perm(t + 4);
+        if (vprev) issue_v(vr);
         const bool kpre = t + 2 < nt;
-        if (kpre) issue_k(tile_key0(t + 2), kbuf == 0 ? 2 : kbuf - 1);
+        if (kpre) issue_k(kr, kbuf == 0 ? 2 : kbuf - 1);
+        // rows for the next iteration: V of tile t, K of tile t+3 (its ring
+        // slot was filled during iteration t-1)
+        tile_rows(kb0, t, vr);
+        if (t + 3 < nt) tile_rows(tile_key0(t + 3), t + 3, kr);
 
         int my_need = 0;
         float alpha = 1.f;
@@ -914,17 +975,16 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             palpha = alpha;
         }
         if (lane == 0 && my_need) atomicOr(&need[kbuf], 1u << wave);
-        // K of tile t+1 has landed (that of t+2 may be in flight); V reads and
-        // the need flags are complete
+        // K of tile t+1 and the source rows of tile t+4 have landed (K of t+2
+        // may be in flight); V reads and the need flags are complete
         if (kpre) dma_wait<DI>();
         else dma_wait<0>();
         lds_wait();
         tile_barrier();
-        prev_kb0 = kb0;
         kbuf = kbuf == 2 ? 0 : kbuf + 1;
     }
     if (nt > 0 && any_need(kbuf == 0 ? 2 : kbuf - 1)) {
-        issue_v(prev_kb0);
+        issue_v(vr);
         dma_wait<0>();
         tile_barrier();
         if (pend) apply_pending();
@@ -934,10 +994,10 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     float l_lo, l_hi;
     swap32(l_part, l_lo, l_hi);
     const float l_tot = l_lo + l_hi;
-    if (row_valid) {
+    if (row_valid && uint32_t(qsrc) < uint32_t(N)) {  // entries of perm outside 0..N-1 store nothing
         const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
         if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
-        float* orow = a.o + int64_t(bh) * N * D + int64_t(qrow) * D;
+        float* orow = a.o + (int64_t(bh) * N + qsrc) * D;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -990,7 +1050,7 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
     for (int t = tid; t < B * D; t += 256) {
         const int rr = t / D, dd = t % D;
         const int64_t qq = int64_t(qb) * B + rr;
-        Qs[rr][dd] = qq < N ? __uint_as_float(uint32_t(Qh[qq * D + dd]) << 16) : 0.f;
+        Qs[rr][dd] = qq < N ? __uint_as_float(uint32_t(Qh[src_row(a.perm, qq, N) * D + dd]) << 16) : 0.f;
     }
     float m = -INFINITY, l = 0.f;
     float O[D / B];
@@ -1015,8 +1075,9 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
         for (int t = tid; t < B * D; t += 256) {
             const int rr = t / D, dd = t % D;
             const int64_t key = kb0 + rr;
-            Ks[rr][dd] = key < N ? __uint_as_float(uint32_t(Kh[key * D + dd]) << 16) : 0.f;
-            Vs[rr][dd] = key < N ? __uint_as_float(uint32_t(Vh[key * D + dd]) << 16) : 0.f;
+            const int64_t src = key < N ? src_row(a.perm, key, N) : 0;
+            Ks[rr][dd] = key < N ? __uint_as_float(uint32_t(Kh[src * D + dd]) << 16) : 0.f;
+            Vs[rr][dd] = key < N ? __uint_as_float(uint32_t(Vh[src * D + dd]) << 16) : 0.f;
         }
         __syncthreads();
         const int64_t key = kb0 + c;
@@ -1063,8 +1124,9 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
     if (valid) {
         const float inv = 1.0f / l;
         if (l == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
+        const int64_t qsrc = src_row(a.perm, qrow, N);
 #pragma unroll
-        for (int u = 0; u < D / B; ++u) Oh[qrow * D + c + B * u] = O[u] * inv;
+        for (int u = 0; u < D / B; ++u) Oh[qsrc * D + c + B * u] = O[u] * inv;
     }
     if (a.counters && tid == 0) {
         atomicAdd(&a.counters[0], (unsigned long long)(e1 > e0 ? e1 - e0 : 0));
@@ -1093,18 +1155,21 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
         else hipLaunchKernelGGL((k_flash_mfma<64, 128>), grid, block, 0, stream, a);
     } else {
         const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
-        if (a.bk == 64) {
-            if (lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL(k_flash_lam<128>, pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL(k_flash_lam<64>, pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+        auto go = [&](auto gather) {
+            constexpr bool G = decltype(gather)::value;
+            if (a.bk == 64 && lam_on) {
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_lam<128, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_lam<64, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+            } else if (a.bk == 64) {
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             } else {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 2, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             }
-        } else {
-            if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            else hipLaunchKernelGGL((k_flash_dma<64, 2, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-        }
+        };
+        if (a.perm) go(std::true_type{});
+        else go(std::false_type{});
     }
     return hipGetLastError();
 }

@@ -14,6 +14,7 @@
 //   k_csr          per group: row offsets from the group totals, then the
 //                  ascending column lists from the mask rows (ballot compaction).
 #include <cfloat>
+#include <type_traits>
 
 #include "sa_internal.h"
 
@@ -98,10 +99,13 @@ __device__ inline void wave_lds_sync() {
 // loads are issued before any is consumed.  Squared norms come from the
 // bf16 dot-product instruction (exact products, fp32 accumulation) and are
 // summed over the CH lanes of a row with DPP; the per-row-slot sums are
-// reduced across the wave once at the end.
-template <int D>
+// reduced across the wave once at the end.  GATHER: q and k stay in the
+// original token order and row r of the reordered sequence is perm[r]; the
+// source rows of the next step are loaded while the current one is consumed.
+template <int D, bool GATHER>
 __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k, int64_t N,
+                                                     const uint16_t* __restrict__ k,
+                                                     const int32_t* __restrict__ perm, int64_t N,
                                                      int bq, int bk, int64_t q_blocks, int64_t all_blocks,
                                                      int n_qb, int n_kb, float* __restrict__ qbar,
                                                      float* __restrict__ kbar, float* __restrict__ simq,
@@ -121,9 +125,24 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
     const int j = int(local - bh * nb);
     const int64_t t0 = int64_t(j) * b;
     const int len = int(min(int64_t(b), N - t0));
-    const uint16_t* src = (is_q ? q : k) + (bh * N + t0) * D;
+    const uint16_t* src = (is_q ? q : k) + (bh * N + (GATHER ? 0 : t0)) * D;
     const int ch = lane % CH;
     const int slot = lane / CH;
+    // source rows of one step (rows past the block repeat its last row and are masked)
+    auto step_rows = [&](int r0, int (&sr)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(r0 + u * RPW + slot, len - 1);
+            if constexpr (GATHER) {
+                const int32_t p = perm[t0 + r];
+                sr[u] = (p >= 0 && p < N) ? p : 0;  // an entry outside 0..N-1 reads row 0
+            } else {
+                sr[u] = r;
+            }
+        }
+    };
+    int sr[U];
+    step_rows(0, sr);
 
     float ax[8], au[8];
 #pragma unroll
@@ -134,10 +153,11 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * RPW + slot;
             // streamed once: nontemporal, so the block rows do not displace cached data
-            const u32x4* p = reinterpret_cast<const u32x4*>(src + int64_t(min(r, len - 1)) * D) + ch;
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + int64_t(sr[u]) * D) + ch;
             const u32x4 v = __builtin_nontemporal_load(p);
             raw[u] = r < len ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
         }
+        if (r0 + U * RPW < len) step_rows(r0 + U * RPW, sr);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
@@ -678,20 +698,25 @@ __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, c
 
 int64_t topcdf_groups(int64_t bh, int64_t n_qb) { return bh * ((n_qb + kGroupRows - 1) / kGroupRows); }
 
-hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const PredictShape& s, float* qbar,
-                              float* kbar, float* simq, float* simk, int32_t* dev_status,
+hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
+                              float* qbar, float* kbar, float* simq, float* simk, int32_t* dev_status,
                               hipStream_t stream) {
     const int64_t qb = int64_t(s.B) * s.Hq * s.n_qb;
     const int64_t kb = int64_t(s.B) * s.Hkv * s.n_kb;
     const int64_t wgs = (qb + kb + 3) / 4;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid{unsigned(wgs), 1, 1};
-    if (s.D == 128)
-        hipLaunchKernelGGL(k_block_stats<128>, grid, dim3(256), 0, stream, q, k, s.N, s.bq, s.bk, qb, qb + kb,
-                           int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
-    else
-        hipLaunchKernelGGL(k_block_stats<64>, grid, dim3(256), 0, stream, q, k, s.N, s.bq, s.bk, qb, qb + kb,
-                           int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
+    auto go = [&](auto gather) {
+        constexpr bool G = decltype(gather)::value;
+        if (s.D == 128)
+            hipLaunchKernelGGL((k_block_stats<128, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.bq, s.bk, qb,
+                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
+        else
+            hipLaunchKernelGGL((k_block_stats<64, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.bq, s.bk, qb,
+                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
+    };
+    if (perm) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 

@@ -53,7 +53,8 @@ struct TopCdfArgs {
     float scale;
 };
 
-hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const PredictShape& s,
+// perm: token permutation (q and k in the original order), or null
+hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk,
                               int32_t* dev_status, hipStream_t stream);
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream);
@@ -70,6 +71,7 @@ struct FlashArgs {
     float* o;
     const int32_t* row_ptr;
     const int32_t* col_idx;
+    const int32_t* perm;  // token permutation (q, k, v, o in the original order), or null
     uint8_t* pv_skip;
     unsigned long long* counters;
     int32_t* dev_status;

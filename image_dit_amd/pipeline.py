@@ -1,5 +1,9 @@
 """One call of the whole path: reorder -> predict mask -> sparse attention -> inverse reorder.
 
+Two equivalent forms: ``run`` materialises the reordered q, k, v (three
+permute calls), predicts, attends and undoes the reorder on O; ``run_fused``
+passes the permutation to the gather entry points instead, which read q, k, v
+in the original order and write O there, with bit-identical results.
 Torch only allocates device memory and supplies the stream; every step runs
 in the HIP library through the C ABI (``_lib``).
 """
@@ -73,7 +77,8 @@ def config_from_workload(w, sparsity="default") -> PathConfig:
 class SparseAttentionPath:
     """Owns the device buffers of one workload shape and runs the four entry points."""
 
-    def __init__(self, cfg: PathConfig, device="cuda", col_cap: Optional[int] = None, want_skip=True):
+    def __init__(self, cfg: PathConfig, device="cuda", col_cap: Optional[int] = None, want_skip=True,
+                 materialize=True):
         import torch
 
         self.cfg = cfg
@@ -82,9 +87,10 @@ class SparseAttentionPath:
         self.perm = torch.from_numpy(self.perm_host).to(device)
         bf = torch.bfloat16
         B, Hq, Hkv, N, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.D
-        self.qp = torch.empty((B, Hq, N, D), dtype=bf, device=device)
-        self.kp = torch.empty((B, Hkv, N, D), dtype=bf, device=device)
-        self.vp = torch.empty((B, Hkv, N, D), dtype=bf, device=device)
+        # reordered copies (only for the materialising form)
+        self.qp = torch.empty((B, Hq, N, D), dtype=bf, device=device) if materialize else None
+        self.kp = torch.empty((B, Hkv, N, D), dtype=bf, device=device) if materialize else None
+        self.vp = torch.empty((B, Hkv, N, D), dtype=bf, device=device) if materialize else None
         self.mp = cfg.mask_params()
         ws_bytes = L.sa_predict_workspace_bytes(self.mp)
         if ws_bytes == 0:
@@ -100,7 +106,7 @@ class SparseAttentionPath:
         self.pv_skip = (torch.empty(max(self.col_cap, 1) * self.groups, dtype=torch.uint8, device=device)
                         if want_skip else None)
         self.counters = torch.zeros(3, dtype=torch.int64, device=device)
-        self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
+        self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device) if materialize else None
         self.o = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
 
     # --- the four steps (each one C-ABI call, or three for the permute) ---
@@ -126,6 +132,22 @@ class SparseAttentionPath:
         self.predict(stream=stream)
         self.attend(stream)
         self.unpermute(stream)
+        return self.o
+
+    # --- the fused form: the reorder is an index map inside the two kernels' loads ---
+    def predict_gather(self, q, k, mask_out=None, sim_q=None, sim_k=None, stream=None):
+        L.sa_predict_mask_gather(q, k, self.perm, self.mp, self.ws, self.row_ptr,
+                                 self.col_idx[:self.col_cap] if self.col_cap > 0 else self.col_idx[:0],
+                                 self.status[0:1], mask_out, sim_q, sim_k, stream)
+
+    def attend_gather(self, q, k, v, stream=None):
+        L.sa_sparse_attn_fwd_gather(q, k, v, self.perm, self.o, self.ap, self.row_ptr, self.col_idx,
+                                    self.status[1:2], self.pv_skip, self.counters, stream)
+
+    def run_fused(self, q, k, v, stream=None):
+        """q, k, v: bf16 in the original token order; returns O (fp32) in the original order."""
+        self.predict_gather(q, k, stream=stream)
+        self.attend_gather(q, k, v, stream)
         return self.o
 
     # --- inspection helpers (host copies, for tests and reports) ---

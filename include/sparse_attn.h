@@ -206,10 +206,37 @@ int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* 
  * (G = ceil(block_q/32) flags per CSR entry, col_cap entries)
  * with pv_skip[e*G + g] = 1 when group g skipped the PV of CSR entry e;
  * counters device int64 [3] = {QK block products, PV group-blocks executed,
- * PV group-blocks skipped}, reset by the call. */
+ * PV group-blocks skipped}, reset by the call.
+ * N * D * 2 must be below 2^31 (one head of k or v under 2 GiB), else
+ * SA_ERR_UNSUPPORTED. */
 int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
                        const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
                        uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream);
+
+/* The reorder folded into the two calls above, as an index map instead of a
+ * copy (reordering is a relabelling of the tokens: "AIGC 基本功|视频稀疏注意力的
+ * 误差与布局-SparseAttn", section 3.4).  q, k and v are in the ORIGINAL token
+ * order; perm_dev (device int32 [N], as written by sa_plan_permutation) gives
+ * position i of the reordered sequence as token perm_dev[i].
+ *   sa_predict_mask_gather(q, k, perm, ...) == sa_predict_mask on
+ *     q'[b,h,i,:] = q[b,h,perm[i],:], k' likewise (bf16 inputs only): the same
+ *     CSR, mask and similarities, indexed by reordered blocks, bit for bit.
+ *   sa_sparse_attn_fwd_gather(q, k, v, perm, o, ...) == sa_sparse_attn_fwd on
+ *     q', k', v' followed by sa_unpermute: o is written in the original order,
+ *     o[b,h,perm[i],:] = o'[b,h,i,:], bit for bit.
+ * perm_dev must be a permutation of 0..N-1.  This is not checked; an entry
+ * outside 0..N-1 never makes a kernel access memory outside q, k, v and o,
+ * but the results are then unspecified.
+ * Other arguments, errors and outputs as in the non-gather calls; perm_dev must
+ * not be NULL. */
+int sa_predict_mask_gather(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                           const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr,
+                           int32_t* col_idx, int64_t col_cap, uint8_t* mask_out, float* sim_q,
+                           float* sim_k, int32_t* dev_status, void* stream);
+int sa_sparse_attn_fwd_gather(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* perm_dev, float* o, const sa_attn_params* p,
+                              const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
+                              int64_t* counters, int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -119,3 +119,21 @@ def test_full_size_sampled_parity(name):
         f"out_max={worst_max:.3e} out_mean={sum_abs / n_el:.3e} pv_exec={cnt[1]} pv_skip={cnt[2]}")
     assert n_bad == 0
     assert worst_max <= R.MAX_ABS and sum_abs / n_el <= R.MEAN_ABS
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_gather_form_bit_identical(name):
+    """At full size, the gather form (the one the benchmark times) equals the
+    materialising form bit for bit: CSR, mask, statistics, skip flags,
+    counters and every output element."""
+    from test_gpu_parity import assert_forms_identical, run_both_forms
+    w = CONFIGS[name]
+    log(f"[full-gather] {name}: B={w.B} Hq={w.Hq} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam}")
+    cfg = sa.config_from_workload(w)
+    q, k, v = generate(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del q, k, v
+    a, b = run_both_forms(cfg, qd, kd, vd)
+    assert a["status"] == (sa.SA_OK, sa.SA_OK)
+    assert_forms_identical(a, b)
+    log(f"[full-gather] {name}: nnz={int(a['rp'][-1])} identical")

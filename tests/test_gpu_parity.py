@@ -268,3 +268,68 @@ def test_rerun_is_bitwise_deterministic():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32))
     assert np.array_equal(outs[0][3], outs[1][3])
+
+
+def _bf16_inputs(w):
+    out = []
+    for x in generate(w):
+        out.append(dev(x) if x.dtype == np.uint16 else torch.from_numpy(x).cuda().to(torch.bfloat16))
+    return out
+
+
+def run_both_forms(cfg, qd, kd, vd):
+    """The materialising form (permute, predict, attend, unpermute) and the gather
+    form (predict_gather, attend_gather) on the same bf16 inputs; host copies of
+    everything each writes."""
+    res = []
+    for fused in (False, True):
+        path = sa.SparseAttentionPath(cfg, materialize=not fused)
+        mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
+        simq = torch.zeros(cfg.rows, dtype=torch.float32, device="cuda")
+        simk = torch.zeros(cfg.B * cfg.Hkv * cfg.n_kb, dtype=torch.float32, device="cuda")
+        if fused:
+            path.predict_gather(qd, kd, mask_out=mask, sim_q=simq, sim_k=simk)
+            path.attend_gather(qd, kd, vd)
+        else:
+            path.permute(qd, kd, vd)
+            path.predict(mask_out=mask, sim_q=simq, sim_k=simk)
+            path.attend()
+            path.unpermute()
+        torch.cuda.synchronize()
+        rp, ci = path.csr_host()
+        nnz = int(rp[-1])
+        res.append(dict(
+            status=path.statuses(), rp=rp, ci=ci, mask=mask.cpu().numpy(),
+            simq=simq.cpu().numpy().view(np.uint32), simk=simk.cpu().numpy().view(np.uint32),
+            qbar=path.workspace_view(0, torch.float32, (cfg.B, cfg.Hq, cfg.n_qb, cfg.D)).cpu().numpy().view(np.uint32),
+            kbar=path.workspace_view(1, torch.float32, (cfg.B, cfg.Hkv, cfg.n_kb, cfg.D)).cpu().numpy().view(np.uint32),
+            skip=path.pv_skip[:min(nnz, path.col_cap) * path.groups].cpu().numpy(),
+            counters=path.counters.cpu().numpy(), o=path.o.cpu().numpy().view(np.uint32)))
+        del path
+    return res
+
+
+def assert_forms_identical(a, b):
+    for key in a:
+        x, y = np.asarray(a[key]), np.asarray(b[key])
+        if not np.array_equal(x, y):
+            if x.shape == y.shape and x.ndim == 4:  # o: [B, H, N, D] as uint32 bits
+                neq = x != y
+                rows = neq.any(axis=3)
+                log(f"  {key}: {int(np.count_nonzero(neq))} elements differ in {int(rows.sum())} rows, "
+                    f"first rows {np.argwhere(rows)[:6].tolist()}")
+            assert False, key
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_gather_form_bit_identical(name):
+    """Reading q, k, v through the permutation inside the kernels gives the
+    materialised path's CSR, mask, block statistics, skip flags, counters and
+    outputs bit for bit."""
+    w = SMALL[name]
+    cfg = sa.config_from_workload(w)
+    log(f"[gather] {name}: N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam} causal={w.causal}")
+    qd, kd, vd = _bf16_inputs(w)
+    a, b = run_both_forms(cfg, qd, kd, vd)
+    assert a["status"] == (sa.SA_OK, sa.SA_OK)
+    assert_forms_identical(a, b)

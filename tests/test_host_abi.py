@@ -129,6 +129,24 @@ def test_predict_rejects_invalid_parameters(kw, code):
     p = _mask_params(**kw)
     assert sa.sa_predict_workspace_bytes(p) == 0
     assert _predict_code(p) == code
+    assert _predict_gather_code(p) == code
+
+
+def _predict_gather_code(p, ws_bytes=1 << 30, perm=FAKE, **ptrs):
+    args = dict(q=FAKE, k=FAKE, ws=FAKE, row_ptr=FAKE, col_idx=FAKE, status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_predict_mask_gather(args["q"], args["k"], perm, ctypes.byref(p), args["ws"], ws_bytes,
+                                           args["row_ptr"], args["col_idx"], 100, None, None, None,
+                                           args["status"], None)
+
+
+def test_predict_gather_rejects_bad_buffers():
+    p = _mask_params()
+    need = sa.sa_predict_workspace_bytes(p)
+    assert _predict_gather_code(p, perm=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_gather_code(p, ws_bytes=need - 1) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_gather_code(p, q=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _predict_gather_code(p, k=ctypes.c_void_p((1 << 20) + 2)) == sa.SA_ERR_INVALID_ARGUMENT
 
 
 def test_predict_rejects_bad_buffers():
@@ -175,6 +193,28 @@ def test_attn_rejects_invalid_parameters(kw, code):
     base = dict(B=1, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64)
     base.update(kw)
     assert _attn_code(sa.make_attn_params(**base)) == code
+    assert _attn_gather_code(sa.make_attn_params(**base)) == code
+
+
+def _attn_gather_code(p, perm=FAKE, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, row_ptr=FAKE, col_idx=FAKE, status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_sparse_attn_fwd_gather(args["q"], args["k"], args["v"], perm, args["o"], ctypes.byref(p),
+                                              args["row_ptr"], args["col_idx"], None, None, args["status"], None)
+
+
+def test_attn_gather_rejects_bad_buffers():
+    p = sa.make_attn_params(1, 4, 2, 1000, 128, 128, 64)
+    assert _attn_gather_code(p, perm=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _attn_gather_code(p, v=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _attn_gather_code(p, q=ctypes.c_void_p((1 << 20) + 4)) == sa.SA_ERR_INVALID_ARGUMENT
+
+
+def test_attn_rejects_heads_of_2gib():
+    # a head of k or v is addressed with 32-bit offsets below 2^31 bytes
+    assert _attn_code(sa.make_attn_params(1, 1, 1, (1 << 30) // 128, 128, 128, 64)) == sa.SA_ERR_UNSUPPORTED
+    assert _attn_gather_code(sa.make_attn_params(1, 1, 1, (1 << 30) // 128, 128, 128, 64)) == sa.SA_ERR_UNSUPPORTED
+    assert _attn_code(sa.make_attn_params(1, 1, 1, (1 << 30) // 64, 64, 128, 64)) == sa.SA_ERR_UNSUPPORTED
 
 
 def test_attn_rejects_bad_buffers():
