@@ -498,32 +498,45 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const TileLane<D> tl(wave, lane);
     const int4v rP = head_desc(a.perm, uint32_t(N) * 4u);
     const uint32_t pr_lds = lds_addr(&prow[0][0]);
-    // wave 0 fetches the source rows of tile t into ring slot t % kRing
-    auto issue_perm = [&](int t) {
+    // wave 0 fetches the source rows of tile t (first key key0) into ring slot t % kRing
+    auto issue_perm = [&](int t, int key0) {
         if constexpr (GATHER) {
-            const int key0 = tile_key0(t);
             if (wave == 0 && key0 >= 0)
                 dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4), uint32_t(key0 + lane) * 4u);
         }
     };
-    // byte offsets of this lane's two source rows of tile t; an invalid tile
-    // or a row past the end gets an offset beyond the buffer (reads zeros)
-    auto tile_rows = [&](int t, uint32_t (&rb)[2]) {
-        const int key0 = tile_key0(t);
+    // A tile's rows for this lane: its first key and the ring entries of the
+    // lane's two rows (GATHER), read one iteration before the DMA and turned
+    // into byte offsets only there, so the LDS read latency is hidden.
+    struct Rows {
+        int key0;
+        int32_t src[2];
+    };
+    auto tile_rows = [&](int t, int key0, Rows& rw) {
+        rw.key0 = key0;
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) rw.src[x] = prow[t % kRing][tl.r0 + 8 * x];
+        }
+    };
+    // byte offsets of the two source rows; an invalid tile or a row past the
+    // end gets an offset beyond the buffer (reads zeros)
+    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2]) {
         if constexpr (GATHER) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                const bool ok = key0 >= 0 && key0 + r < N;
-                rb[x] = ok ? uint32_t(prow[t % kRing][r]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < N) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
             }
         } else {
-            const uint32_t base = key0 < 0 ? 0x80000000u : uint32_t(key0) * uint32_t(D * 2);
+            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
 #pragma unroll
             for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
         }
     };
-    auto issue_kv = [&](const uint32_t (&rb)[2], auto KN) {
+    auto issue_kv = [&](const Rows& rw, auto KN) {
+        uint32_t rb[2];
+        row_bytes(rw, rb);
         const uint32_t kl = lds_addr(kbuf_of(KN)) + uint32_t(wave * DI * 1024);
         const uint32_t vl = lds_addr(vbuf_of(KN)) + uint32_t(wave * DI * 1024);
 #pragma unroll
@@ -553,15 +566,19 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const float c2 = a.scale * kLog2e;
     int n_exec = 0;
     bool bad_col = false;
-    uint32_t nr[2];  // source rows of the next tile to fetch
+    Rows nr;  // rows of the next tile to fetch
+    // first keys of tiles t, t+1, t+2 (one column index is loaded per step,
+    // ahead of the ring reads, so waiting for it never waits for them)
+    int kc = nt > 0 ? tile_key0(0) : -1, k1 = nt > 1 ? tile_key0(1) : -1, k2 = nt > 2 ? tile_key0(2) : -1;
 
     // tile t: K and V in buffer KC; tile t+1 goes to buffer KN
     auto step = [&](int t, auto KC, auto KN) {
-        const int kb0 = tile_key0(t);
-        if (GATHER && t + 3 < nt) issue_perm(t + 3);
+        const int kb0 = kc;
+        const int k3 = t + 3 < nt ? tile_key0(t + 3) : -1;
+        if (GATHER && t + 3 < nt) issue_perm(t + 3, k3);
         if (t + 1 < nt) issue_kv(nr, KN);
         // ring slot t+2 was filled during iteration t-1
-        if (t + 2 < nt) tile_rows(t + 2, nr);
+        if (t + 2 < nt) tile_rows(t + 2, k2, nr);
         if (kb0 < 0) {
             bad_col = true;
         } else if (wave_rows) {
@@ -642,21 +659,26 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         // operand reads of tile t are complete (consumed by the MFMAs)
         dma_wait<0>();
         tile_barrier();  // ... everyone's; the buffers of tile t are free again
+        kc = k1;
+        k1 = k2;
+        k2 = k3;
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     if constexpr (GATHER) {
-        for (int t = 0; t < 3 && t < nt; ++t) issue_perm(t);
+        issue_perm(0, kc);
+        issue_perm(1, k1);
+        issue_perm(2, k2);
         dma_wait<0>();
         tile_barrier();
     }
     if (nt > 0) {
-        uint32_t rb[2];
-        tile_rows(0, rb);
-        issue_kv(rb, I0{});
+        Rows r0;
+        tile_rows(0, kc, r0);
+        issue_kv(r0, I0{});
     }
-    if (nt > 1) tile_rows(1, nr);
+    if (nt > 1) tile_rows(1, k1, nr);
     dma_wait<0>();
     __syncthreads();
     q_ready(qf);
@@ -772,37 +794,52 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const uint32_t pr_lds = lds_addr(&prow[0][0]);
     const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DI * 1024);
     const uint32_t vs_lds = lds_addr(&Vs[0]) + uint32_t(wave * DI * 1024);
-    // wave 0 fetches the source rows of tile t into ring slot t % kRing
-    auto issue_perm = [&](int t) {
+    // wave 0 fetches the source rows of tile t (first key key0) into ring slot t % kRing
+    auto issue_perm = [&](int t, int key0) {
         if constexpr (GATHER) {
-            const int key0 = tile_key0(t);
             if (wave == 0 && key0 >= 0)
                 dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4), uint32_t(key0 + lane) * 4u);
         }
     };
-    // byte offsets of this lane's two source rows of the tile starting at
-    // key0 (tile t); an invalid tile or a row past the end gets an offset
-    // beyond the buffer (reads zeros)
-    auto tile_rows = [&](int key0, int t, uint32_t (&rb)[2]) {
+    // A tile's rows for this lane: its first key and the ring entries of the
+    // lane's two rows (GATHER), read one iteration before the DMA and turned
+    // into byte offsets only there, so the LDS read latency is hidden.
+    struct Rows {
+        int key0;
+        int32_t src[2];
+    };
+    auto tile_rows = [&](int key0, int t, Rows& rw) {
+        rw.key0 = key0;
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) rw.src[x] = prow[t % kRing][tl.r0 + 8 * x];
+        }
+    };
+    // byte offsets of the two source rows; an invalid tile or a row past the
+    // end gets an offset beyond the buffer (reads zeros)
+    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2]) {
         if constexpr (GATHER) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                const bool ok = key0 >= 0 && key0 + r < N;
-                rb[x] = ok ? uint32_t(prow[t % kRing][r]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < N) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
             }
         } else {
-            const uint32_t base = key0 < 0 ? 0x80000000u : uint32_t(key0) * uint32_t(D * 2);
+            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
 #pragma unroll
             for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
         }
     };
-    auto issue_k = [&](const uint32_t (&rb)[2], int buf) {  // this wave's share of a K tile
+    auto issue_k = [&](const Rows& rw, int buf) {  // this wave's share of a K tile
+        uint32_t rb[2];
+        row_bytes(rw, rb);
 #pragma unroll
         for (int c = 0; c < DI; ++c)
             dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), tl.k_off(rb, c));
     };
-    auto issue_v = [&](const uint32_t (&rb)[2]) {  // this wave's share of a V tile
+    auto issue_v = [&](const Rows& rw) {  // this wave's share of a V tile
+        uint32_t rb[2];
+        row_bytes(rw, rb);
 #pragma unroll
         for (int c = 0; c < DI; ++c) dma16_at(rV, vs_lds + uint32_t(c * 1024), tl.v_off(rb, c));
     };
@@ -856,42 +893,50 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 
     // kr: source rows of the next K tile to fetch (t+2 during iteration t);
     // vr: those of tile t-1, whose V may be fetched during iteration t
-    uint32_t kr[2], vr[2];
+    Rows kr, vr;
+    // first keys of tiles t .. t+3 (one column index is loaded per iteration,
+    // ahead of the ring reads, so waiting for it never waits for them)
+    int kc = nt > 0 ? tile_key0(0) : -1, k1 = nt > 1 ? tile_key0(1) : -1;
+    int k2 = nt > 2 ? tile_key0(2) : -1, k3 = nt > 3 ? tile_key0(3) : -1;
     if constexpr (GATHER) {
-        for (int t = 0; t < 4 && t < nt; ++t) issue_perm(t);
+        issue_perm(0, kc);
+        issue_perm(1, k1);
+        issue_perm(2, k2);
+        issue_perm(3, k3);
         dma_wait<0>();
         tile_barrier();
     }
     if (nt > 0) {
-        tile_rows(tile_key0(0), 0, kr);
+        tile_rows(kc, 0, kr);
         issue_k(kr, 0);
     }
     if (nt > 1) {
-        tile_rows(tile_key0(1), 1, kr);
+        tile_rows(k1, 1, kr);
         issue_k(kr, 1);
     }
-    if (nt > 2) tile_rows(tile_key0(2), 2, kr);
+    if (nt > 2) tile_rows(k2, 2, kr);
     if (tid < 3) need[tid] = 0u;
     dma_wait<0>();
     __syncthreads();
     q_ready(qf);
     int kbuf = 0;  // t % 3, also the need slot of tile t
     for (int t = 0; t < nt; ++t) {
-        const int kb0 = tile_key0(t);
+        const int kb0 = kc;
+        const int k4 = t + 4 < nt ? tile_key0(t + 4) : -1;
         const int slot_prev = kbuf == 0 ? 2 : kbuf - 1;  // (t - 1) % 3
         const int slot_next = kbuf == 2 ? 0 : kbuf + 1;  // (t + 1) % 3 == (t - 2) % 3
         // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
         const bool vprev = t > 0 && any_need(slot_prev);
         // the mask of tile t-2 was read during iteration t-1: clear it for tile t+1
         if (tid == 0) need[slot_next] = 0u;
-        if (GATHER && t + 4 < nt) issue_perm(t + 4);
+        if (GATHER && t + 4 < nt) issue_perm(t + 4, k4);
         if (vprev) issue_v(vr);
         const bool kpre = t + 2 < nt;
         if (kpre) issue_k(kr, kbuf == 0 ? 2 : kbuf - 1);
         // rows for the next iteration: V of tile t, K of tile t+3 (its ring
         // slot was filled during iteration t-1)
         tile_rows(kb0, t, vr);
-        if (t + 3 < nt) tile_rows(tile_key0(t + 3), t + 3, kr);
+        if (t + 3 < nt) tile_rows(k3, t + 3, kr);
 
         int my_need = 0;
         float alpha = 1.f;
@@ -982,6 +1027,10 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         lds_wait();
         tile_barrier();
         kbuf = kbuf == 2 ? 0 : kbuf + 1;
+        kc = k1;
+        k1 = k2;
+        k2 = k3;
+        k3 = k4;
     }
     if (nt > 0 && any_need(kbuf == 0 ? 2 : kbuf - 1)) {
         issue_v(vr);
