@@ -7,7 +7,7 @@
 //                  HBM-bound: every byte of Q and K is read exactly once.
 //   k_topcdf       per group of 16 query blocks of one head: compressed
 //                  scores against every key-block mean on the fp32 matrix
-//                  cores, then per query block (one wavefront each) the
+//                  cores, then per query block (a wavefront takes two) the
 //                  guard/sink/window forcing, the softmax over the candidates,
 //                  an exact radix selection for TopCdf and the keep floor, the
 //                  dense mask row, its kept count and the group's total.
@@ -207,9 +207,14 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
 // ---------------------------------------------------------------- TopCdf
 constexpr int kGroupRows = 16;  // query blocks per workgroup: the N side of the score MFMA
 
-// Row stride (floats) of the LDS score tile: a multiple of 64 plus 4, so the
-// 16 rows written by one float4 store land on 16 different bank quads.
-inline int score_stride(int n_kb) { return (n_kb + 63) / 64 * 64 + 4; }
+// Row stride (floats) of the LDS score tile: room for every key block plus a
+// pad, an odd number of 16-byte quads, so the 16 rows written by one float4
+// store land on 16 different bank quads.
+inline int score_stride(int n_kb) {
+    int ls = (n_kb + 3) / 4 * 4 + 4;
+    if ((ls / 4) % 2 == 0) ls += 4;
+    return ls;
+}
 
 struct RowGeom {
     int nv;        // valid key blocks (prefix 0..nv-1)
@@ -329,7 +334,7 @@ __device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pr
 // over the radix digits of the keys (the TopCdf search carries the mass per
 // bin, the floor search the count), so no sort is needed.  Returns the row's
 // kept count.
-__device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, const uint8_t* colf,
+__device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, const uint32_t* colf,
                           uint32_t* hS, int lane) {
     const RowGeom g = row_geom(a, i);
     const int64_t grow = int64_t(bh) * a.n_qb + i;
@@ -343,12 +348,12 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
     for (int q = lane; 4 * q < nv; q += 64) {
         uint4 x = row4[q];
         uint32_t* xs = reinterpret_cast<uint32_t*>(&x);
-        const uint32_t cf = reinterpret_cast<const uint32_t*>(colf)[q];
+        const uint32_t cf = (colf[q >> 3] >> ((4 * q) & 31)) & 0xfu;  // blocks 4q .. 4q+3
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int j = 4 * q + t;
             if (j < nv) {
-                const bool f = ((cf >> (8 * t)) & 0xffu) || (a.causal && causal_forced(a, g, j));
+                const bool f = ((cf >> t) & 1u) || (a.causal && causal_forced(a, g, j));
                 if (f) {
                     xs[t] = kForcedKey;
                     ++nf;
@@ -514,15 +519,17 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
     return cnt;
 }
 
-// Dynamic LDS: scores[16][ls] f32 | per wave: histogram[256] u32 | column
-// forcing flags[n_kb] u8.
+// Eight wavefronts per group of 16 query blocks; wavefront w selects query
+// blocks 2w and 2w+1.  Dynamic LDS: scores[16][ls] f32 | per wavefront:
+// histogram[256] u32 | column forcing bits[ceil(n_kb/32)] u32.
+constexpr int kTopcdfWaves = 8;
 template <int D>
-__global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
+__global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int32_t wave_tot[4];
+    __shared__ int32_t wave_tot[kTopcdfWaves];
     float* scores = reinterpret_cast<float*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(scores + kGroupRows * ls);
-    uint8_t* colf = reinterpret_cast<uint8_t*>(hist + 4 * 256);
+    uint32_t* colf = hist + kTopcdfWaves * 256;
 
     const int groups = (a.n_qb + kGroupRows - 1) / kGroupRows;
     const int bh = blockIdx.x / groups;  // b * Hq + hq
@@ -538,15 +545,22 @@ __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
     const int i_last = min(i0 + kGroupRows, a.n_qb) - 1;
     const int ncols = row_geom(a, i_last).nv;  // columns any row of the group can see
 
-    for (int j = threadIdx.x; j < ncols; j += 256) colf[j] = column_forced(a, j, simk[j]) ? 1 : 0;
+    // column forcing as bits: word j/32 of the mask, one ballot per 64 blocks
+    for (int j0 = 64 * wave; j0 < ncols; j0 += 64 * kTopcdfWaves) {
+        const int j = j0 + lane;
+        const unsigned long long f = __ballot(j < ncols && column_forced(a, j, simk[j]));
+        if (lane == 0) {
+            colf[j0 >> 5] = uint32_t(f);
+            colf[(j0 >> 5) + 1] = uint32_t(f >> 32);
+        }
+    }
 
     // ---- compressed scores on v_mfma_f32_16x16x4_f32: A = 16 key-block means
     // (rows), B = the group's 16 query-block means (columns).  Lane l feeds
     // operand slot l/16 of row/column l%16; head-dim entry 16c + 4(l/16) + e
     // goes to step (c, e), so each lane reads float4s of contiguous entries.
     // The result lands as query row l%16, key blocks 4(l/16)..+3 of the tile.
-    // Tiles t and t+4 of a wave alternate between two register buffers, so
-    // the next tile's loads are in flight during the current tile's MFMAs.
+    // One operand buffer per wavefront: 24 wavefronts per CU hide the loads.
     {
         constexpr int C = D / 16;
         const int r16 = lane & 15;
@@ -556,12 +570,11 @@ __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
 #pragma unroll
         for (int c = 0; c < C; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qs + 16 * c);
         const int ntile = (ncols + 15) >> 4;
-        auto load_k = [&](f32x4 (&kv)[C], int t) {
+        for (int t = wave; t < ntile; t += kTopcdfWaves) {
+            f32x4 kv[C];
             const float* ks = kbar + int64_t(min(t * 16 + r16, ncols - 1)) * D + 4 * sub;
 #pragma unroll
             for (int c = 0; c < C; ++c) kv[c] = *reinterpret_cast<const f32x4*>(ks + 16 * c);
-        };
-        auto tile = [&](const f32x4 (&kv)[C], int t) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < C; c += 2)
@@ -570,33 +583,28 @@ __global__ __launch_bounds__(256) void k_topcdf(TopCdfArgs a, int ls) {
                     acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c][e], qv[c][e], acc0, 0, 0, 0);
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c + 1][e], qv[c + 1][e], acc1, 0, 0, 0);
                 }
-            const f32x4 s = (acc0 + acc1) * a.scale;
-            *reinterpret_cast<f32x4*>(scores + r16 * ls + t * 16 + 4 * sub) = s;
-        };
-        f32x4 ka[C], kb[C];
-        if (wave < ntile) load_k(ka, wave);
-        if (wave + 4 < ntile) load_k(kb, wave + 4);
-        for (int t = wave; t < ntile; t += 8) {
-            tile(ka, t);
-            if (t + 8 < ntile) load_k(ka, t + 8);
-            if (t + 4 < ntile) {
-                tile(kb, t + 4);
-                if (t + 12 < ntile) load_k(kb, t + 12);
-            }
+            const f32x4 sc = (acc0 + acc1) * a.scale;
+            // blocks past the row's room (the last tile's tail) are not stored
+            if (t * 16 + 4 * sub < ls) *reinterpret_cast<f32x4*>(scores + r16 * ls + t * 16 + 4 * sub) = sc;
         }
     }
     __syncthreads();
 
     uint32_t* hS = hist + wave * 256;
     int tot = 0;
-    for (int rr = wave; rr < kGroupRows; rr += 4) {
+    for (int rr = 2 * wave; rr < 2 * wave + 2; ++rr) {
         const int i = i0 + rr;
         if (i >= a.n_qb) break;
         tot += select_row(a, bh, i, reinterpret_cast<uint32_t*>(scores + rr * ls), colf, hS, lane);
     }
     if (lane == 0) wave_tot[wave] = tot;
     __syncthreads();
-    if (threadIdx.x == 0) a.group_tot[blockIdx.x] = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    if (threadIdx.x == 0) {
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < kTopcdfWaves; ++w) sum += wave_tot[w];
+        a.group_tot[blockIdx.x] = sum;
+    }
 }
 
 // ---------------------------------------------------------------- CSR
@@ -723,14 +731,16 @@ hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream) {
     if (a.n_kb > SA_MAX_KEY_BLOCKS) return hipErrorInvalidValue;
     const int ls = score_stride(a.n_kb);
-    const size_t lds = size_t(kGroupRows) * ls * 4 + size_t(4) * 256 * 4 + size_t(a.n_kb + 15) / 16 * 16;
+    // column bits: whole 64-block ballots
+    const size_t lds = size_t(kGroupRows) * ls * 4 + size_t(kTopcdfWaves) * 256 * 4 + size_t(a.n_kb + 63) / 64 * 8;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t nwg = topcdf_groups(int64_t(a.B) * a.Hq, a.n_qb);
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 block{64 * kTopcdfWaves, 1, 1};
     if (a.D == 128)
-        hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), dim3(256), lds, stream, a, ls);
+        hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), block, lds, stream, a, ls);
     else
-        hipLaunchKernelGGL(k_topcdf<64>, dim3(unsigned(nwg)), dim3(256), lds, stream, a, ls);
+        hipLaunchKernelGGL(k_topcdf<64>, dim3(unsigned(nwg)), block, lds, stream, a, ls);
     return hipGetLastError();
 }
 
