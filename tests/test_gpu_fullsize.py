@@ -8,6 +8,7 @@ mask (bit-exact), the counters against the CSR and skip flags, and the
 outputs of sampled query blocks against fp64 on the GPU's CSR.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -25,7 +26,13 @@ import _ref as R  # noqa: E402
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-FULL = ["image", "video", "long_video", "causal_long"]
+# the four workloads at full size, plus one head at the largest supported
+# key-block count (n_kb = SA_MAX_KEY_BLOCKS = 2048, 64-key blocks over 131072
+# tokens): with PV skip on the Hilbert-ordered field, and causal without it
+FULL_W = {name: CONFIGS[name] for name in ["image", "video", "long_video", "causal_long"]}
+FULL_W["max_blocks_lam"] = dataclasses.replace(CONFIGS["long_video"], Hq=1, Hkv=1, latent=(2, 256, 256), seed=81)
+FULL_W["max_blocks_causal"] = dataclasses.replace(CONFIGS["causal_long"], Hq=2, Hkv=1, block_k=64, seed=82)
+FULL = list(FULL_W)
 
 
 def log(*a):
@@ -39,7 +46,7 @@ def dev(x):
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_parity(name):
-    w = CONFIGS[name]
+    w = FULL_W[name]
     log(f"[full] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k}")
     q, k, v = generate(w)
     cfg = sa.config_from_workload(w)
@@ -115,6 +122,8 @@ def test_full_size_sampled_parity(name):
             if w.lam is not None:
                 far, _ = R.lambda_disagreements(recs[i], w.lam)
                 assert far == 0
+    if name.startswith("max_blocks"):
+        assert cfg.n_kb == sa.SA_MAX_KEY_BLOCKS
     log(f"[full] {name}: nnz={int(rp[-1])} sampled_rows={n_rows} mismatch={n_bad} borderline={n_border} "
         f"out_max={worst_max:.3e} out_mean={sum_abs / n_el:.3e} pv_exec={cnt[1]} pv_skip={cnt[2]}")
     assert n_bad == 0
@@ -127,7 +136,7 @@ def test_full_size_gather_form_bit_identical(name):
     materialising form bit for bit: CSR, mask, statistics, skip flags,
     counters and every output element."""
     from test_gpu_parity import assert_forms_identical, run_both_forms
-    w = CONFIGS[name]
+    w = FULL_W[name]
     log(f"[full-gather] {name}: B={w.B} Hq={w.Hq} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam}")
     cfg = sa.config_from_workload(w)
     q, k, v = generate(w)

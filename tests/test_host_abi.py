@@ -124,12 +124,18 @@ def _predict_code(p, ws_bytes=1 << 30, **ptrs):
     (dict(scale=-1.0), sa.SA_ERR_INVALID_ARGUMENT),
     (dict(D=96), sa.SA_ERR_UNSUPPORTED),
     (dict(N=4096 * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),  # more key blocks than supported
+    (dict(N=sa.SA_MAX_KEY_BLOCKS * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),  # one block past the limit
 ])
 def test_predict_rejects_invalid_parameters(kw, code):
     p = _mask_params(**kw)
     assert sa.sa_predict_workspace_bytes(p) == 0
     assert _predict_code(p) == code
     assert _predict_gather_code(p) == code
+
+
+def test_predict_accepts_the_largest_key_block_count():
+    p = _mask_params(N=sa.SA_MAX_KEY_BLOCKS * 64, block_k=64)
+    assert sa.sa_predict_workspace_bytes(p) > 0
 
 
 def _predict_gather_code(p, ws_bytes=1 << 30, perm=FAKE, **ptrs):
