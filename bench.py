@@ -216,26 +216,30 @@ def main():
         run_step()
     torch.cuda.synchronize()
 
+    # One event before each stage that launches work, nothing else: a stage
+    # ends where the next recorded one starts (the last stage of a step at the
+    # next step's first event, or at `end`).  Every recorded event is a queue
+    # marker that leaves the GPU idle for a few microseconds, so the gather
+    # form records two per step (before the prediction, before the attention).
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    real = [j for j, (name, _) in enumerate(stages) if not (gather and name in ("permute", "unpermute"))]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in real] for _ in range(K)]
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record(stream)
     for s in range(K):
-        e = ev[s]
-        for j, (_, f) in enumerate(stages):
-            e[j].record(stream)
-            f()
-        e[4].record(stream)
+        for x, j in enumerate(real):
+            ev[s][x].record(stream)
+            stages[j][1]()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
+    total_ms = ev[0][0].elapsed_time(end)
     stage = np.zeros(4)
-    for e in ev:
-        for j in range(4):
-            stage[j] += e[j].elapsed_time(e[j + 1])
+    for s in range(K):
+        for x, j in enumerate(real):
+            nxt = ev[s][x + 1] if x + 1 < len(real) else (ev[s + 1][0] if s + 1 < K else end)
+            stage[j] += ev[s][x].elapsed_time(nxt)
     stage /= K
     ms_step = total_ms / K
 
