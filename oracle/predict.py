@@ -21,6 +21,10 @@ silent or garbled:
   blocks included; TopCdf may keep more.
 * sinks: key blocks touching the first ``sink_front`` or the last
   ``sink_back`` tokens are kept by every query block.
+* sink rows (the other reading of the first-frame sink, where the first frame
+  takes part in full attention as queries too): a query block touching the
+  first ``sink_rows`` tokens keeps its whole valid row, as a low-similarity
+  query block does.
 * causal: a key block is valid if its first token is not after the query
   block's last token; the window W keeps every valid block holding a key within
   W-1 tokens before the query block's first token; the query block's own
@@ -51,6 +55,7 @@ class MaskParams:
     theta: Optional[float] = None
     sparsity: Optional[float] = None
     scale: Optional[float] = None
+    sink_rows: int = 0
 
     @property
     def n_qb(self):
@@ -127,8 +132,9 @@ def predict_row(i: int, logits_row: np.ndarray, simq_i: float, simk: np.ndarray,
         if abs(simq_i - p.theta) <= THETA_BORDER or \
                 np.any(np.abs(simk[valid] - p.theta) <= THETA_BORDER):
             info["border"].add("theta")
-    # a low-similarity query block computes its whole valid row
-    if p.theta is not None and p.theta > 0 and simq_i < p.theta:
+    # a low-similarity query block computes its whole valid row, and so does
+    # a query block touching the first sink_rows tokens
+    if (p.theta is not None and p.theta > 0 and simq_i < p.theta) or i * p.block_q < p.sink_rows:
         info["forced_row"] = True
         return valid.copy(), info
     cand = valid & ~forced

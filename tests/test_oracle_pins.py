@@ -390,6 +390,28 @@ def test_predicted_mask_p1_head0_is_spatial():
     assert int(tok.sum()) == 1024
 
 
+def test_sink_rows_make_full_rows_of_the_first_frame():
+    """MindIE-SD first-frame sink read as full rows: query blocks touching the first
+    sink_rows tokens keep their whole valid row; the other rows stay the spatial mask."""
+    q, k, v, _, _ = p1_demo_inputs()
+    eye = np.eye(4, dtype=bool)
+    for sink_rows, full in ((0, []), (16, [0]), (17, [0, 1]), (64, [0, 1, 2, 3])):
+        p = P.MaskParams(N=64, block_q=16, block_k=16, tau=0.9, theta=0.5, sink_rows=sink_rows)
+        out = P.predict_head(q[0], k[0], p)
+        want = eye.copy()
+        want[full] = True
+        assert np.array_equal(out["mask"], want), sink_rows
+        assert [i for i in range(4) if out["info"][i]["forced_row"]] == full
+    # causal: the whole valid row of query block 0 is block 0 alone
+    p = P.MaskParams(N=64, block_q=16, block_k=16, causal=True, tau=0.9, theta=0.5, sink_rows=16)
+    out = P.predict_head(q[0], k[0], p)
+    assert np.array_equal(out["mask"][0], [True, False, False, False])
+    # query block 1 is no sink row: its diagonal block is forced and block 0, its only
+    # candidate, holds all the compressed mass
+    assert np.array_equal(out["mask"][1], [True, True, False, False])
+    assert not out["info"][1]["forced_row"]
+
+
 def test_predicted_mask_p1_head1_pixel_major_is_temporal():
     """p1 demo head 1 after the pixel-major reorder, b=4 -> the 16 diagonal tiles (256 pairs)."""
     q, k, v, _, pixel = p1_demo_inputs()
