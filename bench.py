@@ -119,7 +119,7 @@ def cpu_baseline(w, path, q, k, v, budget_s):
     vp = OL.permute_rows(ON.bf16_to_f64(v[0, h]), perm)
     mp = OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal, window=w.window_tokens,
                        sink_front=w.sink_front, sink_back=w.sink_back, tau=w.tau, theta=w.theta,
-                       sparsity=cfg.sparsity)
+                       sparsity=cfg.sparsity, sink_rows=w.sink_rows)
     t0 = time.perf_counter()
     OP.predict_head(qp, kp, mp)
     t_pred = time.perf_counter() - t0

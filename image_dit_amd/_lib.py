@@ -40,7 +40,7 @@ class SaLayout(ctypes.Structure):
 class SaMaskParams(ctypes.Structure):
     _fields_ = [("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32), ("N", c_int64),
                 ("block_q", c_int32), ("block_k", c_int32), ("causal", c_int32),
-                ("reserved0", c_int32), ("window", c_int64), ("sink_front", c_int64),
+                ("sink_rows", c_int32), ("window", c_int64), ("sink_front", c_int64),
                 ("sink_back", c_int64), ("tau", c_double), ("theta", c_double),
                 ("sparsity", c_double), ("scale", c_float), ("reserved1", c_int32)]
 
@@ -153,8 +153,9 @@ def sa_unpermute(y, x, perm, stream=None):
 
 
 def make_mask_params(B, Hq, Hkv, N, D, block_q, block_k, causal=False, window=0, sink_front=0,
-                     sink_back=0, tau=None, theta=None, sparsity=None, scale=0.0) -> SaMaskParams:
-    return SaMaskParams(B, Hq, Hkv, D, N, block_q, block_k, int(causal), 0, window, sink_front,
+                     sink_back=0, tau=None, theta=None, sparsity=None, scale=0.0,
+                     sink_rows=0) -> SaMaskParams:
+    return SaMaskParams(B, Hq, Hkv, D, N, block_q, block_k, int(causal), sink_rows, window, sink_front,
                         sink_back, -1.0 if tau is None else tau, 0.0 if theta is None else theta,
                         -1.0 if sparsity is None else sparsity, scale, 0)
 

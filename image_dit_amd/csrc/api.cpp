@@ -21,7 +21,8 @@ int validate_predict(const sa_mask_params* p) {
     if (p->block_q <= 0 || p->block_k <= 0 || p->block_q > 256 || p->block_k > 256)
         return SA_ERR_INVALID_ARGUMENT;
     if (p->causal != 0 && p->causal != 1) return SA_ERR_INVALID_ARGUMENT;
-    if (p->reserved0 != 0 || p->reserved1 != 0) return SA_ERR_INVALID_ARGUMENT;
+    if (p->reserved1 != 0) return SA_ERR_INVALID_ARGUMENT;
+    if (p->sink_rows < 0 || p->sink_rows > p->N) return SA_ERR_INVALID_ARGUMENT;
     if (p->window < 0 || (p->window > 0 && !p->causal)) return SA_ERR_INVALID_ARGUMENT;
     if (p->sink_front < 0 || p->sink_back < 0 || p->sink_front > p->N || p->sink_back > p->N)
         return SA_ERR_INVALID_ARGUMENT;
@@ -167,7 +168,7 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
     a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.N = s.N;
     a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb);
     a.causal = p->causal; a.window = p->window;
-    a.sink_front = p->sink_front; a.sink_back = p->sink_back;
+    a.sink_front = p->sink_front; a.sink_back = p->sink_back; a.sink_rows = p->sink_rows;
     a.tau_d = p->tau;
     a.tau = float(p->tau);
     a.theta = p->theta > 0.0 ? float(p->theta) : 0.0f;

@@ -338,7 +338,8 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
                           uint32_t* hS, int lane) {
     const RowGeom g = row_geom(a, i);
     const int64_t grow = int64_t(bh) * a.n_qb + i;
-    const bool forced_row = a.theta > 0.f && a.simq[grow] < a.theta;
+    // low-similarity query blocks and sink rows keep their whole valid row
+    const bool forced_row = (a.theta > 0.f && a.simq[grow] < a.theta) || g.q_first < a.sink_rows;
     const int nv = g.nv;
     uint4* row4 = reinterpret_cast<uint4*>(row);
 

@@ -46,6 +46,7 @@ struct TopCdfArgs {
     int n_qb, n_kb;
     int causal;
     int64_t window, sink_front, sink_back;
+    int64_t sink_rows;  // query blocks touching tokens [0, sink_rows) keep their whole valid row
     float tau;       // < 0: unset
     double tau_d;    // tau as given, for the >= 1 test
     float theta;     // <= 0: off

@@ -33,6 +33,7 @@ class PathConfig:
     causal: bool = False
     window_tokens: int = 0
     sink_front: int = 0
+    sink_rows: int = 0
     sink_back: int = 0
     tau: Optional[float] = None
     theta: Optional[float] = None
@@ -55,7 +56,7 @@ class PathConfig:
     def mask_params(self):
         return L.make_mask_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
                                   self.causal, self.window_tokens, self.sink_front, self.sink_back,
-                                  self.tau, self.theta, self.sparsity, self.scale)
+                                  self.tau, self.theta, self.sparsity, self.scale, self.sink_rows)
 
     def attn_params(self, col_cap=0):
         return L.make_attn_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
@@ -70,7 +71,8 @@ def config_from_workload(w, sparsity="default") -> PathConfig:
     return PathConfig(B=w.B, Hq=w.Hq, Hkv=w.Hkv, N=w.N, D=w.D, block_q=w.block_q, block_k=w.block_k,
                       order=w.order, latent=w.latent, window=w.window, txt_len=w.txt_len,
                       first_frame_sink=w.first_frame_sink, causal=w.causal, window_tokens=w.window_tokens,
-                      sink_front=w.sink_front, sink_back=w.sink_back, tau=w.tau, theta=w.theta,
+                      sink_front=w.sink_front, sink_back=w.sink_back, sink_rows=getattr(w, "sink_rows", 0),
+                      tau=w.tau, theta=w.theta,
                       sparsity=w.sparsity if sparsity == "default" else sparsity, lam=w.lam)
 
 

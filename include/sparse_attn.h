@@ -90,7 +90,9 @@ typedef struct sa_mask_params {
     int64_t N;                /* tokens per sequence */
     int32_t block_q, block_k; /* b_q, b_k (tokens per query / key block), 1..256 */
     int32_t causal;           /* 0 or 1 */
-    int32_t reserved0;        /* must be 0 */
+    int32_t sink_rows;        /* query blocks touching tokens [0, sink_rows) keep their whole
+                                 valid row (MindIE-SD first-frame sink, read as full rows);
+                                 0 = off, at most N */
     int64_t window;           /* causal sliding window W in tokens (0 = off; needs causal) */
     int64_t sink_front;       /* key blocks touching tokens [0, sink_front) are always kept */
     int64_t sink_back;        /* key blocks touching tokens [N-sink_back, N) are always kept */
@@ -168,7 +170,8 @@ int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
  *   3. forced key blocks (within the valid set): key similarity < theta; sink
  *      blocks; causal: window blocks (last key >= first query - W + 1) and the
  *      blocks overlapping the query block;
- *   4. query similarity < theta: the whole valid row is kept;
+ *   4. query similarity < theta, or a query block touching the first
+ *      sink_rows tokens: the whole valid row is kept;
  *   5. otherwise the other valid blocks are candidates: scores
  *      qbar.kbar*scale, softmax over the candidates, sorted by probability
  *      descending then block index ascending; TopCdf keeps the blocks whose

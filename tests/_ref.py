@@ -36,6 +36,7 @@ def mask_params(w, sparsity="default") -> OP.MaskParams:
     s = w.sparsity if sparsity == "default" else sparsity
     return OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal,
                          window=w.window_tokens, sink_front=w.sink_front, sink_back=w.sink_back,
+                         sink_rows=w.sink_rows,
                          tau=w.tau, theta=w.theta, sparsity=s)
 
 

@@ -42,6 +42,9 @@ SMALL = {
     "image_s_lam": rep(CONFIGS["image"], Hq=3, Hkv=3, latent=(1, 20, 37), lam=-8.0, seed=61),
     "causal_s64_lam": rep(CONFIGS["causal_long"], Hq=2, Hkv=1, latent=(1, 1, 777), window_tokens=300,
                           block_k=64, lam=-8.0, seed=71),
+    # the first frame (16x24 tokens, three query blocks) as full rows as well as sink columns
+    "video_s_sink_rows": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20,
+                             sink_front=16 * 24, sink_back=20, sink_rows=16 * 24, seed=91),
 }
 
 
@@ -119,7 +122,10 @@ def test_path_parity(name):
             assert np.allclose(gsimq[r0:r0 + cfg.n_qb], ref["simq"], rtol=1e-5, atol=1e-5)
             kb0 = (b * w.Hkv + hk) * cfg.n_kb
             assert np.allclose(gsimk[kb0:kb0 + cfg.n_kb], ref["simk"], rtol=1e-5, atol=1e-5)
-            # (a3) predicted mask
+            # (a3) predicted mask; sink rows are whole valid rows on the GPU too
+            for i in range(cfg.n_qb):
+                if i * w.block_q < w.sink_rows:
+                    assert np.array_equal(gmask[r0 + i], OP._valid_blocks(i, mp)), i
             bad, border, checked = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref)
             n_bad += len(bad)
             n_border += len(border)

@@ -125,6 +125,8 @@ def _predict_code(p, ws_bytes=1 << 30, **ptrs):
     (dict(D=96), sa.SA_ERR_UNSUPPORTED),
     (dict(N=4096 * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),  # more key blocks than supported
     (dict(N=sa.SA_MAX_KEY_BLOCKS * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),  # one block past the limit
+    (dict(sink_rows=-1), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(sink_rows=1001), sa.SA_ERR_INVALID_ARGUMENT),  # more than N tokens
 ])
 def test_predict_rejects_invalid_parameters(kw, code):
     p = _mask_params(**kw)

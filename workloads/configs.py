@@ -50,6 +50,7 @@ class Workload:
     window_tokens: int = 0        # causal sliding window W in tokens (0 = off)
     sink_front: int = 0           # tokens at the front of the permuted order kept as sinks
     sink_back: int = 0            # tokens at the back of the permuted order kept as sinks
+    sink_rows: int = 0            # tokens at the front whose query blocks keep their whole row
     tau: Optional[float] = None   # TopCdf cumulative mass (None = unset)
     theta: Optional[float] = None  # self-similarity guard (None = off)
     sparsity: Optional[float] = None  # keep floor (None = unset)
