@@ -109,6 +109,60 @@ def plan_permutation(n_tokens: int, order: int, latent=(1, 1, 1), window=(1, 1, 
     return perm
 
 
+def token_tiles(n_tokens: int, latent, txt_len: int, first_frame_sink: bool, tile) -> np.ndarray:
+    """3-D tile of every token in the ORIGINAL order, shape (n_tokens, 3); -1 rows for
+    tokens outside the tiling (text, and frame 0 when it is the first-frame sink).
+
+    A video token at latent (t, h, w) lies in tile ((t - t0) // tile_t, h // tile_h,
+    w // tile_w), t0 = 1 with the first-frame sink (the frames that take part in the
+    reorder are tiled from their own first frame), else 0.
+    """
+    t, h, w = latent
+    if min(t, h, w) <= 0 or txt_len < 0 or n_tokens != txt_len + t * h * w:
+        raise ValueError("n_tokens must equal txt_len + t*h*w")
+    if min(tile) <= 0:
+        raise ValueError("tile extents must be positive")
+    t0 = 1 if first_frame_sink else 0
+    out = np.full((n_tokens, 3), -1, dtype=np.int64)
+    for x in range(txt_len, n_tokens):
+        e = x - txt_len
+        tt, rem = divmod(e, h * w)
+        hh, ww = divmod(rem, w)
+        if tt < t0:
+            continue
+        out[x] = ((tt - t0) // tile[0], hh // tile[1], ww // tile[2])
+    return out
+
+
+def plan_tile_window(n_tokens: int, order: int, latent, window, txt_len: int, first_frame_sink: bool,
+                     tile, radius, block_q: int, block_k: int) -> np.ndarray:
+    """3-D tile-window pattern of blocks in the permuted order (bool [n_qb, n_kb]).
+
+    The sliding-tile idea of the SparseAttn article (its discussion of Sliding Tile
+    Attention: one query tile shares one set of key tiles): query block i and key block
+    j are paired when some query token of i and some key token of j lie in tiles that
+    differ by at most radius[a] along every axis a.  Untiled tokens pair with nothing.
+    """
+    if min(radius) < 0:
+        raise ValueError("radii must be non-negative")
+    perm = plan_permutation(n_tokens, order, latent, window, txt_len, first_frame_sink)
+    tiles = token_tiles(n_tokens, latent, txt_len, first_frame_sink, tile)[perm]
+    n_qb = -(-n_tokens // block_q)
+    n_kb = -(-n_tokens // block_k)
+
+    def block_tiles(b, i):
+        rows = tiles[i * b:min((i + 1) * b, n_tokens)]
+        return {tuple(r) for r in rows.tolist() if r[0] >= 0}
+
+    qt = [block_tiles(block_q, i) for i in range(n_qb)]
+    kt = [block_tiles(block_k, j) for j in range(n_kb)]
+    out = np.zeros((n_qb, n_kb), dtype=bool)
+    for i in range(n_qb):
+        for j in range(n_kb):
+            out[i, j] = any(all(abs(a[d] - c[d]) <= radius[d] for d in range(3)) for a in qt[i] for c in kt[j])
+    return out
+
+
 def permute_rows(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
     """y[..., i, :] = x[..., perm[i], :]"""
     return np.take(x, perm, axis=-2)

@@ -21,6 +21,8 @@ silent or garbled:
   blocks included; TopCdf may keep more.
 * sinks: key blocks touching the first ``sink_front`` or the last
   ``sink_back`` tokens are kept by every query block.
+* a forced block pattern (e.g. the 3-D tile windows of ``layout.plan_tile_window``)
+  adds its blocks of row i to the forced blocks (within the valid set).
 * sink rows (the other reading of the first-frame sink, where the first frame
   takes part in full attention as queries too): a query block touching the
   first ``sink_rows`` tokens keeps its whole valid row, as a low-similarity
@@ -56,6 +58,7 @@ class MaskParams:
     sparsity: Optional[float] = None
     scale: Optional[float] = None
     sink_rows: int = 0
+    forced: Optional[np.ndarray] = None  # bool [n_qb, n_kb]: blocks every head keeps
 
     @property
     def n_qb(self):
@@ -117,6 +120,8 @@ def _forced_blocks(i: int, p: MaskParams, simk: np.ndarray, valid: np.ndarray) -
         if p.window > 0:
             forced |= (k_end - 1) >= q_first - p.window + 1
         forced |= (k_first < q_end) & (k_end > q_first)
+    if p.forced is not None:
+        forced |= np.asarray(p.forced[i], dtype=bool)
     return forced & valid
 
 

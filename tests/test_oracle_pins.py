@@ -412,6 +412,49 @@ def test_sink_rows_make_full_rows_of_the_first_frame():
     assert not out["info"][1]["forced_row"]
 
 
+def test_forced_pattern_blocks_are_kept_and_counted():
+    """A forced block pattern joins the forced blocks: always kept, counted by the floor."""
+    q, k, v, _, _ = p1_demo_inputs()
+    forced = np.zeros((4, 4), dtype=bool)
+    forced[0, 3] = forced[2, 1] = True
+    p = P.MaskParams(N=64, block_q=16, block_k=16, tau=0.9, theta=0.5, forced=forced)
+    out = P.predict_head(q[0], k[0], p)
+    assert np.array_equal(out["mask"], np.eye(4, dtype=bool) | forced)
+    assert out["info"][0]["n_forced"] == 1 and out["info"][1]["n_forced"] == 0
+    # the floor ceil((1-s)|valid|) = 2 is met by the forced block plus the top candidate
+    p = P.MaskParams(N=64, block_q=16, block_k=16, tau=1e-9, theta=0.5, sparsity=0.5, forced=forced)
+    out = P.predict_head(q[0], k[0], p)
+    assert out["mask"][0].sum() == 2 and out["mask"][0][3] and out["mask"][0][0]
+
+
+def test_tile_window_pattern_hand_examples():
+    """Sliding tiles on a 1-D latent of 16 tokens, tiles of 4 = blocks: radius 1 pairs each
+    block with its neighbours (tridiagonal); radius 0 with itself; blocks of 8 tokens hold
+    two tiles each."""
+    tri = np.eye(4, dtype=bool) | np.eye(4, k=1, dtype=bool) | np.eye(4, k=-1, dtype=bool)
+    got = Lay.plan_tile_window(16, Lay.ORDER_IDENTITY, (1, 1, 16), (1, 1, 1), 0, False, (1, 1, 4), (0, 0, 1), 4, 4)
+    assert np.array_equal(got, tri)
+    got = Lay.plan_tile_window(16, Lay.ORDER_IDENTITY, (1, 1, 16), (1, 1, 1), 0, False, (1, 1, 4), (0, 0, 0), 4, 4)
+    assert np.array_equal(got, np.eye(4, dtype=bool))
+    got = Lay.plan_tile_window(16, Lay.ORDER_IDENTITY, (1, 1, 16), (1, 1, 1), 0, False, (1, 1, 4), (0, 0, 0), 8, 4)
+    assert np.array_equal(got, np.array([[1, 1, 0, 0], [0, 0, 1, 1]], dtype=bool))
+    # text (2 tokens, first in the original order) and the first-frame sink are untiled:
+    # with the window order they sit first (frame 0) and last (text); 2 frames of 2x4
+    n = 2 + 3 * 2 * 4
+    tiles = Lay.token_tiles(n, (3, 2, 4), 2, True, (1, 2, 2))
+    assert np.all(tiles[:2] == -1) and np.all(tiles[2:10] == -1)      # text, frame 0
+    assert tuple(tiles[10]) == (0, 0, 0) and tuple(tiles[10 + 8 + 3]) == (1, 0, 1)
+    got = Lay.plan_tile_window(n, Lay.ORDER_WINDOW, (3, 2, 4), (1, 2, 2), 2, True, (1, 2, 2), (0, 0, 0), 4, 4)
+    # permuted order: frame 0 (8 tokens, blocks 0-1), then 4 windows of 4 tokens (blocks 2-5,
+    # one tile each), then text (block 6): only the tiled blocks pair, each with itself
+    want = np.zeros((7, 7), dtype=bool)
+    want[2:6, 2:6] = np.eye(4, dtype=bool)
+    assert np.array_equal(got, want)
+    # a radius covering the whole grid pairs every tiled block with every tiled block
+    got = Lay.plan_tile_window(n, Lay.ORDER_WINDOW, (3, 2, 4), (1, 2, 2), 2, True, (1, 2, 2), (5, 5, 5), 4, 4)
+    assert np.array_equal(got, np.outer(want.any(1), want.any(1)))
+
+
 def test_predicted_mask_p1_head1_pixel_major_is_temporal():
     """p1 demo head 1 after the pixel-major reorder, b=4 -> the 16 diagonal tiles (256 pairs)."""
     q, k, v, _, pixel = p1_demo_inputs()
