@@ -6,7 +6,7 @@ functions raise; there is no fallback path.
 
 import ctypes
 import os
-from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint8, c_void_p
 
 import numpy as np
 
@@ -28,7 +28,8 @@ SA_MAX_KEY_BLOCKS = 2048
 
 EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermute",
            "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
-           "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather")
+           "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather",
+           "sa_plan_tile_window", "sa_predict_mask_ex")
 
 
 class SaLayout(ctypes.Structure):
@@ -94,6 +95,12 @@ def lib() -> ctypes.CDLL:
                                             POINTER(SaAttnParams), c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p]
     L.sa_sparse_attn_fwd_gather.restype = c_int
+    L.sa_plan_tile_window.argtypes = [POINTER(SaLayout)] + [c_int32] * 8 + [POINTER(c_uint8), c_int64, c_int64]
+    L.sa_plan_tile_window.restype = c_int
+    L.sa_predict_mask_ex.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(SaMaskParams), c_void_p,
+                                     c_size_t, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p]
+    L.sa_predict_mask_ex.restype = c_int
     _lib = L
     return L
 
@@ -134,6 +141,18 @@ def sa_plan_permutation(layout: SaLayout) -> np.ndarray:
                                      c_int64(layout.n_tokens))
     _check(code, "sa_plan_permutation")
     return perm
+
+
+def sa_plan_tile_window(layout: SaLayout, tile, radius, block_q: int, block_k: int) -> np.ndarray:
+    """Host-only: the 3-D tile-window block pattern (uint8 [n_qb, n_kb]) in the order
+    sa_plan_permutation gives for the layout."""
+    n = int(layout.n_tokens)
+    n_qb, n_kb = -(-n // block_q), -(-n // block_k)
+    out = np.zeros((n_qb, n_kb), dtype=np.uint8)
+    code = lib().sa_plan_tile_window(ctypes.byref(layout), *(int(x) for x in tile), *(int(x) for x in radius),
+                                     block_q, block_k, out.ctypes.data_as(POINTER(c_uint8)), n_qb, n_kb)
+    _check(code, "sa_plan_tile_window")
+    return out
 
 
 def sa_permute(x, y, perm, stream=None):
@@ -200,6 +219,17 @@ def sa_predict_mask_gather(q, k, perm, p: SaMaskParams, ws, row_ptr, col_idx, de
                                         col_idx.numel(), _ptr(mask_out), _ptr(sim_q), _ptr(sim_k),
                                         _ptr(dev_status), _stream(stream))
     _check(code, "sa_predict_mask_gather")
+
+
+def sa_predict_mask_ex(q, k, perm, forced, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mask_out=None,
+                       sim_q=None, sim_k=None, stream=None):
+    """sa_predict_mask with an optional permutation (None: q, k already reordered) and an
+    optional forced block pattern (device uint8 [n_qb, n_kb], shared by all heads)."""
+    code = lib().sa_predict_mask_ex(_ptr(q), _ptr(k), _ptr(perm), _ptr(forced), ctypes.byref(p), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _ptr(row_ptr), _ptr(col_idx),
+                                    col_idx.numel(), _ptr(mask_out), _ptr(sim_q), _ptr(sim_k),
+                                    _ptr(dev_status), _stream(stream))
+    _check(code, "sa_predict_mask_ex")
 
 
 def sa_sparse_attn_fwd_gather(q, k, v, perm, o, p: SaAttnParams, row_ptr, col_idx, dev_status, pv_skip=None,

@@ -138,9 +138,10 @@ extern "C" int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off
 
 namespace {
 
-int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, const sa_mask_params* p,
-                 void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
-                 uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status, void* stream) {
+int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
+                 const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
+                 int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status,
+                 void* stream) {
     PredictShape s;
     const int st = predict_shape(p, &s);
     if (st != SA_OK) return st;
@@ -164,7 +165,7 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
 
     TopCdfArgs a;
     a.qbar = qbar; a.kbar = kbar; a.simq = simq; a.simk = simk;
-    a.mask = mask; a.counts = counts; a.group_tot = counts + s.rows;
+    a.mask = mask; a.counts = counts; a.group_tot = counts + s.rows; a.forced = forced;
     a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.N = s.N;
     a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb);
     a.causal = p->causal; a.window = p->window;
@@ -228,7 +229,7 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
                                void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
                                int32_t* dev_status, void* stream) {
-    return predict_mask(q, k, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+    return predict_mask(q, k, nullptr, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
                         dev_status, stream);
 }
 
@@ -237,8 +238,16 @@ extern "C" int sa_predict_mask_gather(const uint16_t* q, const uint16_t* k, cons
                                       int32_t* col_idx, int64_t col_cap, uint8_t* mask_out, float* sim_q,
                                       float* sim_k, int32_t* dev_status, void* stream) {
     if (!perm_dev) return SA_ERR_INVALID_ARGUMENT;
-    return predict_mask(q, k, perm_dev, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+    return predict_mask(q, k, perm_dev, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
                         dev_status, stream);
+}
+
+extern "C" int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                                  const uint8_t* forced_dev, const sa_mask_params* p, void* ws, size_t ws_bytes,
+                                  int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, uint8_t* mask_out,
+                                  float* sim_q, float* sim_k, int32_t* dev_status, void* stream) {
+    return predict_mask(q, k, perm_dev, forced_dev, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out,
+                        sim_q, sim_k, dev_status, stream);
 }
 
 extern "C" int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,

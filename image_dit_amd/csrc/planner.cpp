@@ -6,6 +6,8 @@
 // curve variant is J. Skilling, "Programming the Hilbert curve", AIP Conf.
 // Proc. 707 (2004), on the enclosing 2^k cube, axis 0 (t) most significant.
 #include <algorithm>
+#include <climits>
+#include <cstdlib>
 #include <cstdint>
 #include <numeric>
 #include <vector>
@@ -102,5 +104,83 @@ extern "C" int sa_plan_permutation(const sa_layout* L, int32_t* perm, int64_t n)
     std::stable_sort(sel.begin(), sel.end(), [&](int64_t a, int64_t b) { return key[a] < key[b]; });
     for (int64_t e = 0; e < nv; ++e) perm[pos++] = int32_t(orig[sel[e]]);
     for (int64_t k = 0; k < txt; ++k) perm[pos++] = int32_t(k);
+    return SA_OK;
+}
+
+// 3-D tile windows as a block pattern: the sliding-tile idea the SparseAttn
+// article discusses (Sliding Tile Attention: a query tile shares one set of
+// key tiles).  Tiles live on the latent grid of the video tokens that take
+// part in the reorder; query block i and key block j are paired when some of
+// their tokens lie in tiles within the radius along every axis.
+extern "C" int sa_plan_tile_window(const sa_layout* L, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                                   int32_t radius_t, int32_t radius_h, int32_t radius_w, int32_t block_q,
+                                   int32_t block_k, uint8_t* pattern, int64_t n_qb, int64_t n_kb) {
+    if (!L || !pattern || tile_t <= 0 || tile_h <= 0 || tile_w <= 0 || radius_t < 0 || radius_h < 0 ||
+        radius_w < 0 || block_q <= 0 || block_k <= 0)
+        return SA_ERR_INVALID_ARGUMENT;
+    const int64_t n = L->n_tokens;
+    const int64_t T = L->t, H = L->h, W = L->w, txt = L->txt_len;
+    if (n <= 0 || n > INT32_MAX || T <= 0 || H <= 0 || W <= 0 || txt < 0 || txt + T * H * W != n)
+        return SA_ERR_INVALID_ARGUMENT;
+    if (n_qb != (n + block_q - 1) / block_q || n_kb != (n + block_k - 1) / block_k) return SA_ERR_INVALID_ARGUMENT;
+    std::vector<int32_t> perm(static_cast<size_t>(n));
+    const int st = sa_plan_permutation(L, perm.data(), n);
+    if (st != SA_OK) return st;
+    const int64_t t0 = L->first_frame_sink ? 1 : 0;
+    // tile of the token at each permuted position, packed into one integer (-1: untiled)
+    const int64_t nth = (H + tile_h - 1) / tile_h, ntw = (W + tile_w - 1) / tile_w;
+    auto tile_of = [&](int64_t x) -> int64_t {
+        if (x < txt) return -1;
+        const int64_t e = x - txt, t = e / (H * W), h = (e / W) % H, w = e % W;
+        if (t < t0) return -1;
+        return (((t - t0) / tile_t) * nth + h / tile_h) * ntw + w / tile_w;
+    };
+    // distinct tiles of each block, with their bounding box
+    struct BlockTiles {
+        std::vector<int64_t> ids;
+        int64_t lo[3] = {INT64_MAX, INT64_MAX, INT64_MAX}, hi[3] = {-1, -1, -1};
+    };
+    auto collect = [&](int32_t b, int64_t nb) {
+        std::vector<BlockTiles> out(static_cast<size_t>(nb));
+        for (int64_t i = 0; i < nb; ++i) {
+            BlockTiles& bt = out[size_t(i)];
+            for (int64_t p = i * b; p < std::min(n, (i + 1) * b); ++p) {
+                const int64_t id = tile_of(perm[size_t(p)]);
+                if (id < 0) continue;
+                bt.ids.push_back(id);
+                const int64_t c[3] = {id / (nth * ntw), (id / ntw) % nth, id % ntw};
+                for (int a = 0; a < 3; ++a) {
+                    bt.lo[a] = std::min(bt.lo[a], c[a]);
+                    bt.hi[a] = std::max(bt.hi[a], c[a]);
+                }
+            }
+            std::sort(bt.ids.begin(), bt.ids.end());
+            bt.ids.erase(std::unique(bt.ids.begin(), bt.ids.end()), bt.ids.end());
+        }
+        return out;
+    };
+    const std::vector<BlockTiles> qt = collect(block_q, n_qb), kt = collect(block_k, n_kb);
+    const int64_t rad[3] = {radius_t, radius_h, radius_w};
+    for (int64_t i = 0; i < n_qb; ++i) {
+        const BlockTiles& a = qt[size_t(i)];
+        for (int64_t j = 0; j < n_kb; ++j) {
+            const BlockTiles& b = kt[size_t(j)];
+            bool on = false;
+            if (!a.ids.empty() && !b.ids.empty()) {
+                bool boxes = true;  // bounding boxes within the radius: a pair may exist
+                for (int d = 0; d < 3; ++d)
+                    boxes = boxes && a.lo[d] - rad[d] <= b.hi[d] && b.lo[d] - rad[d] <= a.hi[d];
+                for (size_t x = 0; boxes && !on && x < a.ids.size(); ++x) {
+                    const int64_t ca[3] = {a.ids[x] / (nth * ntw), (a.ids[x] / ntw) % nth, a.ids[x] % ntw};
+                    for (size_t y = 0; !on && y < b.ids.size(); ++y) {
+                        const int64_t cb[3] = {b.ids[y] / (nth * ntw), (b.ids[y] / ntw) % nth, b.ids[y] % ntw};
+                        on = std::llabs(ca[0] - cb[0]) <= rad[0] && std::llabs(ca[1] - cb[1]) <= rad[1] &&
+                             std::llabs(ca[2] - cb[2]) <= rad[2];
+                    }
+                }
+            }
+            pattern[i * n_kb + j] = on ? 1 : 0;
+        }
+    }
     return SA_OK;
 }

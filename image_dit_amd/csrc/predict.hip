@@ -344,6 +344,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
     uint4* row4 = reinterpret_cast<uint4*>(row);
 
     // forcing and the candidates' maximum score
+    const uint8_t* fpat = a.forced ? a.forced + int64_t(i) * a.n_kb : nullptr;  // this row of the pattern
     float cmax = -FLT_MAX;
     int nf = 0, nc = 0;
     for (int q = lane; 4 * q < nv; q += 64) {
@@ -354,7 +355,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
         for (int t = 0; t < 4; ++t) {
             const int j = 4 * q + t;
             if (j < nv) {
-                const bool f = ((cf >> t) & 1u) || (a.causal && causal_forced(a, g, j));
+                const bool f = ((cf >> t) & 1u) || (a.causal && causal_forced(a, g, j)) || (fpat && fpat[j]);
                 if (f) {
                     xs[t] = kForcedKey;
                     ++nf;

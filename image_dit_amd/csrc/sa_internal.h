@@ -40,6 +40,7 @@ struct TopCdfArgs {
     uint8_t* mask;
     int32_t* counts;
     int32_t* group_tot;  // kept blocks per group of 16 query blocks
+    const uint8_t* forced;  // [n_qb][n_kb] forced block pattern shared by all heads, or null
     int B, Hq, Hkv, D;
     int64_t N;
     int bq, bk;

@@ -80,7 +80,9 @@ class SparseAttentionPath:
     """Owns the device buffers of one workload shape and runs the four entry points."""
 
     def __init__(self, cfg: PathConfig, device="cuda", col_cap: Optional[int] = None, want_skip=True,
-                 materialize=True):
+                 materialize=True, forced: Optional[np.ndarray] = None):
+        """forced: optional host block pattern [n_qb, n_kb] (nonzero = key block always kept by
+        that query block, in every head), e.g. from ``sa_plan_tile_window``."""
         import torch
 
         self.cfg = cfg
@@ -110,6 +112,12 @@ class SparseAttentionPath:
         self.counters = torch.zeros(3, dtype=torch.int64, device=device)
         self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device) if materialize else None
         self.o = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
+        self.forced = None
+        if forced is not None:
+            forced = np.asarray(forced)
+            if forced.shape != (cfg.n_qb, cfg.n_kb):
+                raise ValueError(f"forced pattern must be [{cfg.n_qb}, {cfg.n_kb}]")
+            self.forced = torch.from_numpy(np.ascontiguousarray(forced != 0).astype(np.uint8)).to(device)
 
     # --- the four steps (each one C-ABI call, or three for the permute) ---
     def permute(self, q, k, v, stream=None):
@@ -117,10 +125,16 @@ class SparseAttentionPath:
         L.sa_permute(k, self.kp, self.perm, stream)
         L.sa_permute(v, self.vp, self.perm, stream)
 
+    def _cols(self):
+        return self.col_idx[:self.col_cap] if self.col_cap > 0 else self.col_idx[:0]
+
     def predict(self, mask_out=None, sim_q=None, sim_k=None, stream=None):
-        L.sa_predict_mask(self.qp, self.kp, self.mp, self.ws, self.row_ptr, self.col_idx[:self.col_cap]
-                          if self.col_cap > 0 else self.col_idx[:0], self.status[0:1], mask_out, sim_q, sim_k,
-                          stream)
+        if self.forced is not None:
+            L.sa_predict_mask_ex(self.qp, self.kp, None, self.forced, self.mp, self.ws, self.row_ptr, self._cols(),
+                                 self.status[0:1], mask_out, sim_q, sim_k, stream)
+            return
+        L.sa_predict_mask(self.qp, self.kp, self.mp, self.ws, self.row_ptr, self._cols(), self.status[0:1],
+                          mask_out, sim_q, sim_k, stream)
 
     def attend(self, stream=None):
         L.sa_sparse_attn_fwd(self.qp, self.kp, self.vp, self.o_perm, self.ap, self.row_ptr, self.col_idx,
@@ -138,8 +152,11 @@ class SparseAttentionPath:
 
     # --- the fused form: the reorder is an index map inside the two kernels' loads ---
     def predict_gather(self, q, k, mask_out=None, sim_q=None, sim_k=None, stream=None):
-        L.sa_predict_mask_gather(q, k, self.perm, self.mp, self.ws, self.row_ptr,
-                                 self.col_idx[:self.col_cap] if self.col_cap > 0 else self.col_idx[:0],
+        if self.forced is not None:
+            L.sa_predict_mask_ex(q, k, self.perm, self.forced, self.mp, self.ws, self.row_ptr, self._cols(),
+                                 self.status[0:1], mask_out, sim_q, sim_k, stream)
+            return
+        L.sa_predict_mask_gather(q, k, self.perm, self.mp, self.ws, self.row_ptr, self._cols(),
                                  self.status[0:1], mask_out, sim_q, sim_k, stream)
 
     def attend_gather(self, q, k, v, stream=None):

@@ -129,6 +129,22 @@ const char* sa_status_string(int code);
  * n must equal L->n_tokens.  Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
 int sa_plan_permutation(const sa_layout* L, int32_t* perm_host, int64_t n);
 
+/* Host only.  3-D tile windows as a forced block pattern (the sliding-tile
+ * idea the SparseAttn article discusses under Sliding Tile Attention: one
+ * query tile shares one set of key tiles).  A video token at latent (t,h,w)
+ * that takes part in the reorder lies in tile ((t-t0)/tile_t, h/tile_h,
+ * w/tile_w), t0 = 1 with first_frame_sink, else 0; text tokens and the sink
+ * frame are untiled.  In the order sa_plan_permutation gives for L (any
+ * order; N must equal txt_len + t*h*w), query block i (block_q tokens) and key
+ * block j (block_k tokens) are paired, pattern_host[i*n_kb + j] = 1, when some
+ * token of i and some token of j lie in tiles that differ by at most
+ * radius_t, radius_h, radius_w along t, h, w; else 0.  n_qb and n_kb must be
+ * ceil(N/block_q) and ceil(N/block_k).  The pattern is an input of
+ * sa_predict_mask_ex.  Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
+int sa_plan_tile_window(const sa_layout* L, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                        int32_t radius_t, int32_t radius_h, int32_t radius_w, int32_t block_q,
+                        int32_t block_k, uint8_t* pattern_host, int64_t n_qb, int64_t n_kb);
+
 /* Row gather with conversion to bf16 (SparseAttn article, section 3.4):
  *   y[b,h,i,:] = bf16_round_nearest_even(x[b,h,perm[i],:])
  * x: device [B,H,N,D] of x_dtype (SA_BF16 or SA_F32); y: device bf16 [B,H,N,D];
@@ -240,6 +256,19 @@ int sa_sparse_attn_fwd_gather(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* perm_dev, float* o, const sa_attn_params* p,
                               const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
                               int64_t* counters, int32_t* dev_status, void* stream);
+
+/* sa_predict_mask with both options in one call: perm_dev as in
+ * sa_predict_mask_gather (NULL: q and k are already in the reordered order),
+ * and forced_dev, a device uint8 [n_qb*n_kb] block pattern shared by every
+ * (batch, head) (NULL: none), e.g. the tile windows of sa_plan_tile_window:
+ * a nonzero entry (i, j) adds key block j to the forced blocks of query
+ * block i (step 3 of sa_predict_mask; valid blocks only), so it is always
+ * kept and counts toward the keep floor.  Other arguments, errors and outputs
+ * as in sa_predict_mask. */
+int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                       const uint8_t* forced_dev, const sa_mask_params* p, void* ws, size_t ws_bytes,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, uint8_t* mask_out,
+                       float* sim_q, float* sim_k, int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

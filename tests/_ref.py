@@ -32,9 +32,17 @@ def permuted(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
     return OL.permute_rows(to_f64(x), perm)
 
 
+def tile_pattern(w):
+    """The oracle's tile-window block pattern of the workload, or None."""
+    if w.tile is None:
+        return None
+    return OL.plan_tile_window(w.N, w.order, w.latent, w.window, w.txt_len, w.first_frame_sink, w.tile,
+                               w.tile_radius, w.block_q, w.block_k)
+
+
 def mask_params(w, sparsity="default") -> OP.MaskParams:
     s = w.sparsity if sparsity == "default" else sparsity
-    return OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal,
+    return OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal, forced=tile_pattern(w),
                          window=w.window_tokens, sink_front=w.sink_front, sink_back=w.sink_back,
                          sink_rows=w.sink_rows,
                          tau=w.tau, theta=w.theta, sparsity=s)

@@ -45,7 +45,18 @@ SMALL = {
     # the first frame (16x24 tokens, three query blocks) as full rows as well as sink columns
     "video_s_sink_rows": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20,
                              sink_front=16 * 24, sink_back=20, sink_rows=16 * 24, seed=91),
+    # 3-D tile windows ([4,8,4] tiles, one tile of reach) forced on top of the prediction
+    "video_s_tiles": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20,
+                         sink_front=16 * 24, sink_back=20, tile=(4, 8, 4), tile_radius=(1, 1, 1), seed=93),
 }
+
+
+def library_tile_pattern(w):
+    """The library's tile-window pattern of the workload (host), or None."""
+    if w.tile is None:
+        return None
+    lay = sa.make_layout(w.N, w.order, w.latent, w.window, w.txt_len, w.first_frame_sink)
+    return sa.sa_plan_tile_window(lay, w.tile, w.tile_radius, w.block_q, w.block_k)
 
 
 def log(*a):
@@ -65,7 +76,7 @@ def host_bits(t):
 
 def run_path(w, sparsity="default"):
     cfg = sa.config_from_workload(w, sparsity)
-    path = sa.SparseAttentionPath(cfg)
+    path = sa.SparseAttentionPath(cfg, forced=library_tile_pattern(w))
     q, k, v = generate(w)
     mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
     simq = torch.zeros(cfg.rows, dtype=torch.float32, device="cuda")
@@ -122,10 +133,13 @@ def test_path_parity(name):
             assert np.allclose(gsimq[r0:r0 + cfg.n_qb], ref["simq"], rtol=1e-5, atol=1e-5)
             kb0 = (b * w.Hkv + hk) * cfg.n_kb
             assert np.allclose(gsimk[kb0:kb0 + cfg.n_kb], ref["simk"], rtol=1e-5, atol=1e-5)
-            # (a3) predicted mask; sink rows are whole valid rows on the GPU too
+            # (a3) predicted mask; sink rows are whole valid rows on the GPU too, and
+            # every block of a forced pattern is kept
             for i in range(cfg.n_qb):
                 if i * w.block_q < w.sink_rows:
                     assert np.array_equal(gmask[r0 + i], OP._valid_blocks(i, mp)), i
+                if mp.forced is not None:
+                    assert np.all(gmask[r0 + i][mp.forced[i] & OP._valid_blocks(i, mp)]), i
             bad, border, checked = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref)
             n_bad += len(bad)
             n_border += len(border)
@@ -283,13 +297,13 @@ def _bf16_inputs(w):
     return out
 
 
-def run_both_forms(cfg, qd, kd, vd):
+def run_both_forms(cfg, qd, kd, vd, forced=None):
     """The materialising form (permute, predict, attend, unpermute) and the gather
     form (predict_gather, attend_gather) on the same bf16 inputs; host copies of
     everything each writes."""
     res = []
     for fused in (False, True):
-        path = sa.SparseAttentionPath(cfg, materialize=not fused)
+        path = sa.SparseAttentionPath(cfg, materialize=not fused, forced=forced)
         mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
         simq = torch.zeros(cfg.rows, dtype=torch.float32, device="cuda")
         simk = torch.zeros(cfg.B * cfg.Hkv * cfg.n_kb, dtype=torch.float32, device="cuda")
@@ -336,6 +350,6 @@ def test_gather_form_bit_identical(name):
     cfg = sa.config_from_workload(w)
     log(f"[gather] {name}: N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam} causal={w.causal}")
     qd, kd, vd = _bf16_inputs(w)
-    a, b = run_both_forms(cfg, qd, kd, vd)
+    a, b = run_both_forms(cfg, qd, kd, vd, forced=library_tile_pattern(w))
     assert a["status"] == (sa.SA_OK, sa.SA_OK)
     assert_forms_identical(a, b)

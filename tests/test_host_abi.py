@@ -88,6 +88,40 @@ def test_planner_rejects_bad_layouts():
     assert code == sa.SA_ERR_INVALID_ARGUMENT
 
 
+TILE_CASES = [
+    # (N, order, latent, window, txt, sink), tile, radius, block_q, block_k
+    ((16, sa.SA_ORDER_IDENTITY, (1, 1, 16), (1, 1, 1), 0, False), (1, 1, 4), (0, 0, 1), 4, 4),
+    ((2 + 3 * 2 * 4, sa.SA_ORDER_WINDOW, (3, 2, 4), (1, 2, 2), 2, True), (1, 2, 2), (0, 0, 1), 4, 4),
+    ((20 + 9 * 16 * 24, sa.SA_ORDER_WINDOW, (9, 16, 24), (4, 8, 4), 20, True), (4, 8, 4), (1, 1, 1), 128, 128),
+    ((9 * 16 * 24, sa.SA_ORDER_WINDOW, (9, 16, 24), (4, 8, 4), 0, False), (4, 8, 4), (0, 1, 2), 128, 64),
+    ((6 * 10 * 21, sa.SA_ORDER_HILBERT, (6, 10, 21), (1, 1, 1), 0, False), (2, 4, 4), (1, 1, 1), 128, 64),
+    ((777, sa.SA_ORDER_IDENTITY, (1, 1, 777), (1, 1, 1), 0, False), (1, 1, 64), (0, 0, 2), 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TILE_CASES)))
+def test_tile_window_planner_matches_oracle(case):
+    (N, order, latent, window, txt, sink), tile, radius, bq, bk = TILE_CASES[case]
+    got = sa.sa_plan_tile_window(sa.make_layout(N, order, latent, window, txt, sink), tile, radius, bq, bk)
+    want = Lay.plan_tile_window(N, order, latent, window, txt, sink, tile, radius, bq, bk)
+    assert got.shape == want.shape
+    assert np.array_equal(got.astype(bool), want)
+
+
+def test_tile_window_planner_rejects_bad_arguments():
+    lay = sa.make_layout(16, sa.SA_ORDER_IDENTITY, (1, 1, 16))
+    for tile, radius in (((0, 1, 4), (0, 0, 1)), ((1, 1, 4), (0, -1, 1))):
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sa_plan_tile_window(lay, tile, radius, 4, 4)
+        assert e.value.code == sa.SA_ERR_INVALID_ARGUMENT
+    with pytest.raises(sa.SparseAttnError):  # the latent must hold every token
+        sa.sa_plan_tile_window(sa.make_layout(16, sa.SA_ORDER_IDENTITY, (1, 1, 8)), (1, 1, 4), (0, 0, 1), 4, 4)
+    out = np.zeros((4, 4), dtype=np.uint8)
+    code = sa.lib().sa_plan_tile_window(ctypes.byref(lay), 1, 1, 4, 0, 0, 1, 4, 4,
+                                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), 4, 3)  # wrong n_kb
+    assert code == sa.SA_ERR_INVALID_ARGUMENT
+
+
 # -------------------------------------------------------------- validation (no device work)
 
 FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every case below fails validation
@@ -133,6 +167,19 @@ def test_predict_rejects_invalid_parameters(kw, code):
     assert sa.sa_predict_workspace_bytes(p) == 0
     assert _predict_code(p) == code
     assert _predict_gather_code(p) == code
+
+
+def test_predict_ex_validates_like_predict():
+    """sa_predict_mask_ex takes the same checks; NULL perm and NULL pattern are allowed."""
+    bad = _mask_params(B=0)
+    good = _mask_params()
+
+    def code(p, q=FAKE, ws=FAKE):
+        return sa.lib().sa_predict_mask_ex(q, FAKE, None, None, ctypes.byref(p), ws, 1 << 30, FAKE, FAKE, 100,
+                                           None, None, None, FAKE, None)
+    assert code(bad) == sa.SA_ERR_INVALID_ARGUMENT
+    assert code(good, q=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert code(good, ws=None) == sa.SA_ERR_INVALID_ARGUMENT
 
 
 def test_predict_accepts_the_largest_key_block_count():

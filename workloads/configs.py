@@ -51,6 +51,8 @@ class Workload:
     sink_front: int = 0           # tokens at the front of the permuted order kept as sinks
     sink_back: int = 0            # tokens at the back of the permuted order kept as sinks
     sink_rows: int = 0            # tokens at the front whose query blocks keep their whole row
+    tile: Optional[Tuple[int, int, int]] = None  # 3-D tile windows forced as blocks (None = off)
+    tile_radius: Tuple[int, int, int] = (0, 0, 0)  # their reach in tiles along t, h, w
     tau: Optional[float] = None   # TopCdf cumulative mass (None = unset)
     theta: Optional[float] = None  # self-similarity guard (None = off)
     sparsity: Optional[float] = None  # keep floor (None = unset)
