@@ -151,8 +151,8 @@ def cpu_baseline(w, path, q, k, v, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards over heads with no communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}); the path would shard over "
+              "(batch, head) with no communication between GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
