@@ -35,12 +35,16 @@ def _block_tokens(cols, bk, N):
 def attend_qblock(q, k, v, i, cols, bq, bk, causal=False, scale=None, lam=None, replay=None):
     """Output rows of query block i given its kept key blocks ``cols`` (ascending).
 
-    q: [N, d], k: [N, d], v: [N, dv] float64 in the permuted order.
+    q: [N, d], k: [Nk, d], v: [Nk, dv] float64 in the permuted order (key blocks cover
+    the Nk keys; Nk = N for self-attention, and must be for causal).
     lam: PV-skip threshold or None.  replay: optional bool array [len(cols), groups]
     forcing the skip decisions (used to compare against another implementation's
     decisions).  Returns (y [rows, dv], record).
     """
     N, d = q.shape
+    Nk = k.shape[0]
+    if causal and Nk != N:
+        raise ValueError("causal attention needs as many keys as queries")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     r0, r1 = i * bq, min((i + 1) * bq, N)
@@ -51,7 +55,7 @@ def attend_qblock(q, k, v, i, cols, bq, bk, causal=False, scale=None, lam=None, 
               "skip": np.zeros((len(cols), ngroups), dtype=bool),
               "gap": np.full((len(cols), ngroups), -np.inf)}
     if lam is None and replay is None:
-        keys = _block_tokens(cols, bk, N)
+        keys = _block_tokens(cols, bk, Nk)
         mask = np.ones((len(rows), len(keys)), dtype=bool)
         if causal:
             mask = keys[None, :] <= rows[:, None]
@@ -66,7 +70,7 @@ def attend_qblock(q, k, v, i, cols, bq, bk, causal=False, scale=None, lam=None, 
         l = np.zeros(len(gr))
         O = np.zeros((len(gr), dv))
         for e, j in enumerate(cols):
-            kt = np.arange(j * bk, min((j + 1) * bk, N))
+            kt = np.arange(j * bk, min((j + 1) * bk, Nk))
             S = (q[gr] @ k[kt].T) * scale
             if causal:
                 S = np.where(kt[None, :] <= gr[:, None], S, -np.inf)

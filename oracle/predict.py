@@ -27,6 +27,9 @@ silent or garbled:
   takes part in full attention as queries too): a query block touching the
   first ``sink_rows`` tokens keeps its whole valid row, as a low-similarity
   query block does.
+* keys of another length: with N_k set, the key blocks cover N_k keys (the
+  MindIE-SD arguments latent_shape_q and latent_shape_k may differ); the back
+  sink counts from the end of the keys.  Causal masks need N_k = N.
 * causal: a key block is valid if its first token is not after the query
   block's last token; the window W keeps every valid block holding a key within
   W-1 tokens before the query block's first token; the query block's own
@@ -59,6 +62,11 @@ class MaskParams:
     scale: Optional[float] = None
     sink_rows: int = 0
     forced: Optional[np.ndarray] = None  # bool [n_qb, n_kb]: blocks every head keeps
+    N_k: Optional[int] = None  # keys per sequence (None: N)
+
+    @property
+    def nk(self):
+        return self.N if self.N_k is None else self.N_k
 
     @property
     def n_qb(self):
@@ -66,7 +74,7 @@ class MaskParams:
 
     @property
     def n_kb(self):
-        return -(-self.N // self.block_k)
+        return -(-self.nk // self.block_k)
 
 
 def block_stats(x: np.ndarray, b: int):
@@ -106,14 +114,14 @@ def _valid_blocks(i: int, p: MaskParams) -> np.ndarray:
 def _forced_blocks(i: int, p: MaskParams, simk: np.ndarray, valid: np.ndarray) -> np.ndarray:
     j = np.arange(p.n_kb)
     k_first = j * p.block_k
-    k_end = np.minimum((j + 1) * p.block_k, p.N)  # one past the block's last token
+    k_end = np.minimum((j + 1) * p.block_k, p.nk)  # one past the block's last token
     forced = np.zeros(p.n_kb, dtype=bool)
     if p.theta is not None and p.theta > 0:
         forced |= simk < p.theta
     if p.sink_front > 0:
         forced |= k_first < p.sink_front
     if p.sink_back > 0:
-        forced |= k_end > p.N - p.sink_back
+        forced |= k_end > p.nk - p.sink_back
     if p.causal:
         q_first = i * p.block_q
         q_end = min((i + 1) * p.block_q, p.N)
@@ -189,6 +197,10 @@ def predict_head(q: np.ndarray, k: np.ndarray, p: MaskParams, rows=None):
     Returns dict(mask [n_qb, n_kb] bool, info list per row, simq, simk, qbar, kbar).
     ``rows`` restricts the work to some query blocks (others stay False).
     """
+    if k.shape[0] != p.nk or q.shape[0] != p.N:
+        raise ValueError("q must hold N tokens and k N_k tokens")
+    if p.causal and p.nk != p.N:
+        raise ValueError("causal masks need as many keys as queries")
     qbar, simq, simq_p = block_stats(q, p.block_q)
     kbar, simk, simk_p = block_stats(k, p.block_k)
     logits = compressed_logits(qbar, kbar, p, q.shape[1])

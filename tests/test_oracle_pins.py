@@ -455,6 +455,33 @@ def test_tile_window_pattern_hand_examples():
     assert np.array_equal(got, np.outer(want.any(1), want.any(1)))
 
 
+def test_keys_of_another_length_duplicated_keys():
+    """Keys of another length (MindIE-SD latent_shape_k != latent_shape_q): repeating every
+    key and value twice leaves dense attention unchanged (each weight halves), and on the
+    p1 demo the predicted row of query block i becomes {i, i+4}: the diagonal block and its
+    copy share its mass (~0.4995 each), so reaching tau = 0.9 takes both, lower index first."""
+    q, k, v, _, _ = p1_demo_inputs()
+    q0, k0, v0 = q[0], k[0], v
+    k2, v2 = np.concatenate([k0, k0]), np.concatenate([v0, v0])
+    for bk in (16, 24):  # 24: a partial last key block
+        n_kb = -(-128 // bk)
+        y2, _ = F.attend_qblock(q0, k2, v2, 1, range(n_kb), 16, bk)
+        y1, _ = F.attend_qblock(q0, k0, v0, 1, range(-(-64 // bk)), 16, bk)
+        assert np.allclose(y2, y1, rtol=1e-12, atol=1e-12)
+    p = P.MaskParams(N=64, N_k=128, block_q=16, block_k=16, tau=0.9, theta=0.5)
+    out = P.predict_head(q0, k2, p)
+    want = np.zeros((4, 8), dtype=bool)
+    for i in range(4):
+        want[i, i] = want[i, i + 4] = True
+    assert np.array_equal(out["mask"], want)
+    # the back sink counts from the end of the keys
+    p = P.MaskParams(N=64, N_k=128, block_q=16, block_k=16, tau=0.9, theta=0.5, sink_back=1)
+    out = P.predict_head(q0, k2, p)
+    assert out["mask"][:, 7].all() and out["info"][0]["n_forced"] == 1
+    with pytest.raises(ValueError):
+        P.predict_head(q0, k2, P.MaskParams(N=64, N_k=128, block_q=16, block_k=16, causal=True, tau=0.9))
+
+
 def test_predicted_mask_p1_head1_pixel_major_is_temporal():
     """p1 demo head 1 after the pixel-major reorder, b=4 -> the 16 diagonal tiles (256 pairs)."""
     q, k, v, _, pixel = p1_demo_inputs()
