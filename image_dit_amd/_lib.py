@@ -43,13 +43,13 @@ class SaMaskParams(ctypes.Structure):
                 ("block_q", c_int32), ("block_k", c_int32), ("causal", c_int32),
                 ("sink_rows", c_int32), ("window", c_int64), ("sink_front", c_int64),
                 ("sink_back", c_int64), ("tau", c_double), ("theta", c_double),
-                ("sparsity", c_double), ("scale", c_float), ("reserved1", c_int32)]
+                ("sparsity", c_double), ("scale", c_float), ("n_keys", c_int32)]
 
 
 class SaAttnParams(ctypes.Structure):
     _fields_ = [("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32), ("Dv", c_int32),
                 ("block_q", c_int32), ("block_k", c_int32), ("causal", c_int32), ("N", c_int64),
-                ("lam", c_float), ("scale", c_float), ("col_cap", c_int64)]
+                ("lam", c_float), ("scale", c_float), ("col_cap", c_int64), ("n_keys", c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -173,16 +173,16 @@ def sa_unpermute(y, x, perm, stream=None):
 
 def make_mask_params(B, Hq, Hkv, N, D, block_q, block_k, causal=False, window=0, sink_front=0,
                      sink_back=0, tau=None, theta=None, sparsity=None, scale=0.0,
-                     sink_rows=0) -> SaMaskParams:
+                     sink_rows=0, n_keys=0) -> SaMaskParams:
     return SaMaskParams(B, Hq, Hkv, D, N, block_q, block_k, int(causal), sink_rows, window, sink_front,
                         sink_back, -1.0 if tau is None else tau, 0.0 if theta is None else theta,
-                        -1.0 if sparsity is None else sparsity, scale, 0)
+                        -1.0 if sparsity is None else sparsity, scale, n_keys)
 
 
 def make_attn_params(B, Hq, Hkv, N, D, block_q, block_k, causal=False, lam=None, scale=0.0,
-                     col_cap=0) -> SaAttnParams:
+                     col_cap=0, n_keys=0) -> SaAttnParams:
     return SaAttnParams(B, Hq, Hkv, D, D, block_q, block_k, int(causal), N,
-                        float("-inf") if lam is None else lam, scale, col_cap)
+                        float("-inf") if lam is None else lam, scale, col_cap, n_keys)
 
 
 def sa_predict_workspace_bytes(p: SaMaskParams) -> int:

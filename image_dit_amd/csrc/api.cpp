@@ -1,6 +1,7 @@
 // C-ABI entry points: synchronous host-side argument checks, workspace
 // carving and kernel orchestration.  No HIP runtime call happens before every
 // argument has been checked, so invalid calls are rejected on any machine.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -21,10 +22,11 @@ int validate_predict(const sa_mask_params* p) {
     if (p->block_q <= 0 || p->block_k <= 0 || p->block_q > 256 || p->block_k > 256)
         return SA_ERR_INVALID_ARGUMENT;
     if (p->causal != 0 && p->causal != 1) return SA_ERR_INVALID_ARGUMENT;
-    if (p->reserved1 != 0) return SA_ERR_INVALID_ARGUMENT;
+    if (p->n_keys < 0 || (p->n_keys != 0 && p->n_keys != p->N && p->causal)) return SA_ERR_INVALID_ARGUMENT;
     if (p->sink_rows < 0 || p->sink_rows > p->N) return SA_ERR_INVALID_ARGUMENT;
     if (p->window < 0 || (p->window > 0 && !p->causal)) return SA_ERR_INVALID_ARGUMENT;
-    if (p->sink_front < 0 || p->sink_back < 0 || p->sink_front > p->N || p->sink_back > p->N)
+    const int64_t nk = p->n_keys > 0 ? p->n_keys : p->N;
+    if (p->sink_front < 0 || p->sink_back < 0 || p->sink_front > nk || p->sink_back > nk)
         return SA_ERR_INVALID_ARGUMENT;
     const bool tau_set = p->tau >= 0.0;
     const bool s_set = p->sparsity >= 0.0;
@@ -36,7 +38,7 @@ int validate_predict(const sa_mask_params* p) {
     if (!(p->theta <= 1.0) || std::isinf(p->theta)) return SA_ERR_INVALID_ARGUMENT;
     if (!std::isfinite(p->scale) || p->scale < 0.0f) return SA_ERR_INVALID_ARGUMENT;
     if (!head_dim_ok(p->D)) return SA_ERR_UNSUPPORTED;
-    const int64_t n_kb = (p->N + p->block_k - 1) / p->block_k;
+    const int64_t n_kb = (nk + p->block_k - 1) / p->block_k;
     if (n_kb > SA_MAX_KEY_BLOCKS) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
@@ -52,7 +54,8 @@ int predict_shape(const sa_mask_params* p, PredictShape* s) {
     s->bq = p->block_q;
     s->bk = p->block_k;
     s->n_qb = (p->N + p->block_q - 1) / p->block_q;
-    s->n_kb = (p->N + p->block_k - 1) / p->block_k;
+    s->Nk = p->n_keys > 0 ? p->n_keys : p->N;
+    s->n_kb = (s->Nk + p->block_k - 1) / p->block_k;
     s->rows = int64_t(p->B) * p->Hq * s->n_qb;
     const int64_t qblk = int64_t(p->B) * p->Hq * s->n_qb;
     const int64_t kblk = int64_t(p->B) * p->Hkv * s->n_kb;
@@ -77,8 +80,11 @@ int validate_attn(const sa_attn_params* p) {
     if (p->col_cap < 0) return SA_ERR_INVALID_ARGUMENT;
     if (!std::isfinite(p->scale) || p->scale < 0.0f) return SA_ERR_INVALID_ARGUMENT;
     if (p->D != p->Dv || !head_dim_ok(p->D)) return SA_ERR_UNSUPPORTED;
-    // one head of k or v is addressed with 32-bit byte offsets below 2^31
-    if (p->N * p->D * 2 >= (int64_t(1) << 31)) return SA_ERR_UNSUPPORTED;
+    if (p->n_keys < 0 || p->n_keys > INT32_MAX || (p->n_keys != 0 && p->n_keys != p->N && p->causal))
+        return SA_ERR_INVALID_ARGUMENT;
+    // one head of q, k or v is addressed with 32-bit byte offsets below 2^31
+    const int64_t nk = p->n_keys > 0 ? p->n_keys : p->N;
+    if (std::max(p->N, nk) * p->D * 2 >= (int64_t(1) << 31)) return SA_ERR_UNSUPPORTED;
     const bool pair_ok = (p->block_q == 16 && p->block_k == 16) ||
                          (p->block_q == 128 && (p->block_k == 64 || p->block_k == 128));
     if (!pair_ok) return SA_ERR_UNSUPPORTED;
@@ -145,6 +151,7 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
     PredictShape s;
     const int st = predict_shape(p, &s);
     if (st != SA_OK) return st;
+    if (perm && s.Nk != s.N) return SA_ERR_UNSUPPORTED;  // one permutation for queries and keys
     if (!q || !k || !ws || !row_ptr || !dev_status || col_cap < 0 || (col_cap > 0 && !col_idx))
         return SA_ERR_INVALID_ARGUMENT;
     if (ws_bytes < s.bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return SA_ERR_INVALID_ARGUMENT;
@@ -167,7 +174,7 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
     a.qbar = qbar; a.kbar = kbar; a.simq = simq; a.simk = simk;
     a.mask = mask; a.counts = counts; a.group_tot = counts + s.rows; a.forced = forced;
     a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.N = s.N;
-    a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb);
+    a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb); a.Nk = s.Nk;
     a.causal = p->causal; a.window = p->window;
     a.sink_front = p->sink_front; a.sink_back = p->sink_back; a.sink_rows = p->sink_rows;
     a.tau_d = p->tau;
@@ -212,9 +219,11 @@ int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     a.counters = reinterpret_cast<unsigned long long*>(counters);
     a.dev_status = dev_status;
     a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.D = p->D; a.N = p->N;
+    a.Nk = p->n_keys > 0 ? p->n_keys : p->N;
+    if (perm && a.Nk != a.N) return SA_ERR_UNSUPPORTED;  // one permutation for queries and keys
     a.bq = p->block_q; a.bk = p->block_k;
     a.n_qb = int((p->N + p->block_q - 1) / p->block_q);
-    a.n_kb = int((p->N + p->block_k - 1) / p->block_k);
+    a.n_kb = int((a.Nk + p->block_k - 1) / p->block_k);
     a.col_cap = p->col_cap;
     a.causal = p->causal;
     a.lambda = p->lambda;

@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     const int hk = hq / (a.Hq / a.Hkv);
     const int64_t N = a.N;
     const uint16_t* Qh = a.q + int64_t(bh) * N * D;
-    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * N * D;
-    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * N * D;
+    const int64_t Nk = a.Nk;
+    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * Nk * D;
+    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * Nk * D;
     float* Oh = a.o + int64_t(bh) * N * D;
 
     const int tid = threadIdx.x;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
         for (int c = tid; c < BK * KCH; c += 256) {
             const int rr = c / KCH, cc = c % KCH;
             uint4 u = make_uint4(0, 0, 0, 0);
-            if (kb0 + rr < N) u = *reinterpret_cast<const uint4*>(Kh + src_row(a.perm, kb0 + rr, N) * D + cc * 8);
+            if (kb0 + rr < Nk) u = *reinterpret_cast<const uint4*>(Kh + src_row(a.perm, kb0 + rr, Nk) * D + cc * 8);
             *reinterpret_cast<uint4*>(Ks + rr * KSTR + cc * 8) = u;
         }
         // ---- V tile, transposed through 4x4 register blocks
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int64_t key = kb0 + kb4 * 4 + rr;
-                rv[rr] = key < N ? *reinterpret_cast<const uint2*>(Vh + src_row(a.perm, key, N) * D + db4 * 4)
+                rv[rr] = key < Nk ? *reinterpret_cast<const uint2*>(Vh + src_row(a.perm, key, Nk) * D + db4 * 4)
                                  : make_uint2(0, 0);
             }
 #pragma unroll
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int64_t key = kb0 + 32 * mt + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool ok = key < N && (!a.causal || key <= qrow);
+                const bool ok = key < Nk && (!a.causal || key <= qrow);
                 const float s = ok ? sacc[mt][i] * c2 : -INFINITY;
                 sacc[mt][i] = s;
                 smax = fmaxf(smax, s);
@@ -458,9 +459,11 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int b = bh / a.Hq;
     const int hk = hq / (a.Hq / a.Hkv);
     const int N = int(a.N);
+    const int Nk = int(a.Nk);  // keys per sequence
     const uint32_t head_bytes = uint32_t(N) * D * 2u;
-    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
-    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const uint32_t kv_bytes = uint32_t(Nk) * D * 2u;
+    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
+    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -526,7 +529,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                rb[x] = (rw.key0 >= 0 && rw.key0 + r < N) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
             }
         } else {
             const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
@@ -594,12 +597,12 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
-            if ((kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0)) {
+            if ((kb0 + BK > Nk) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = kb0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool ok0 = kk < N && (!a.causal || kk <= qrow);
-                    const bool ok1 = kk + 32 < N && (!a.causal || kk + 32 <= qrow);
+                    const bool ok0 = kk < Nk && (!a.causal || kk <= qrow);
+                    const bool ok1 = kk + 32 < Nk && (!a.causal || kk + 32 <= qrow);
                     s0[i] = ok0 ? s0[i] : -INFINITY;
                     s1[i] = ok1 ? s1[i] : -INFINITY;
                 }
@@ -752,9 +755,11 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int b = bh / a.Hq;
     const int hk = hq / (a.Hq / a.Hkv);
     const int N = int(a.N);
+    const int Nk = int(a.Nk);  // keys per sequence
     const uint32_t head_bytes = uint32_t(N) * D * 2u;
-    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
-    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * N * D, head_bytes);
+    const uint32_t kv_bytes = uint32_t(Nk) * D * 2u;
+    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
+    const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -822,7 +827,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                rb[x] = (rw.key0 >= 0 && rw.key0 + r < N) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
             }
         } else {
             const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
@@ -957,12 +962,12 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
-            if ((kb0 + BK > N) || (a.causal && kb0 + BK - 1 > wrow0)) {
+            if ((kb0 + BK > Nk) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = kb0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool ok0 = kk < N && (!a.causal || kk <= qrow);
-                    const bool ok1 = kk + 32 < N && (!a.causal || kk + 32 <= qrow);
+                    const bool ok0 = kk < Nk && (!a.causal || kk <= qrow);
+                    const bool ok1 = kk + 32 < Nk && (!a.causal || kk + 32 <= qrow);
                     s0[i] = ok0 ? s0[i] : -INFINITY;
                     s1[i] = ok1 ? s1[i] : -INFINITY;
                 }
@@ -1088,8 +1093,9 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
     const int hk = hq / (a.Hq / a.Hkv);
     const int64_t N = a.N;
     const uint16_t* Qh = a.q + int64_t(bh) * N * D;
-    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * N * D;
-    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * N * D;
+    const int64_t Nk = a.Nk;
+    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * Nk * D;
+    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * Nk * D;
     float* Oh = a.o + int64_t(bh) * N * D;
 
     const int tid = threadIdx.x;
@@ -1124,15 +1130,15 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
         for (int t = tid; t < B * D; t += 256) {
             const int rr = t / D, dd = t % D;
             const int64_t key = kb0 + rr;
-            const int64_t src = key < N ? src_row(a.perm, key, N) : 0;
-            Ks[rr][dd] = key < N ? __uint_as_float(uint32_t(Kh[src * D + dd]) << 16) : 0.f;
-            Vs[rr][dd] = key < N ? __uint_as_float(uint32_t(Vh[src * D + dd]) << 16) : 0.f;
+            const int64_t src = key < Nk ? src_row(a.perm, key, Nk) : 0;
+            Ks[rr][dd] = key < Nk ? __uint_as_float(uint32_t(Kh[src * D + dd]) << 16) : 0.f;
+            Vs[rr][dd] = key < Nk ? __uint_as_float(uint32_t(Vh[src * D + dd]) << 16) : 0.f;
         }
         __syncthreads();
         const int64_t key = kb0 + c;
         float s = 0.f;
         for (int d = 0; d < D; ++d) s = fmaf(Qs[r][d], Ks[c][d], s);
-        const bool ok = key < N && (!a.causal || key <= qrow);
+        const bool ok = key < Nk && (!a.causal || key <= qrow);
         Ss[r][c] = ok ? s * a.scale : -INFINITY;
         __syncthreads();
         float rmax = -INFINITY;

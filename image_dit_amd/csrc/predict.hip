@@ -105,7 +105,7 @@ __device__ inline void wave_lds_sync() {
 template <int D, bool GATHER>
 __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
-                                                     const int32_t* __restrict__ perm, int64_t N,
+                                                     const int32_t* __restrict__ perm, int64_t N, int64_t Nk,
                                                      int bq, int bk, int64_t q_blocks, int64_t all_blocks,
                                                      int n_qb, int n_kb, float* __restrict__ qbar,
                                                      float* __restrict__ kbar, float* __restrict__ simq,
@@ -124,8 +124,9 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
     const int64_t bh = local / nb;
     const int j = int(local - bh * nb);
     const int64_t t0 = int64_t(j) * b;
-    const int len = int(min(int64_t(b), N - t0));
-    const uint16_t* src = (is_q ? q : k) + (bh * N + (GATHER ? 0 : t0)) * D;
+    const int64_t Ns = is_q ? N : Nk;  // tokens of this side's sequence
+    const int len = int(min(int64_t(b), Ns - t0));
+    const uint16_t* src = (is_q ? q : k) + (bh * Ns + (GATHER ? 0 : t0)) * D;
     const int ch = lane % CH;
     const int slot = lane / CH;
     // source rows of one step (rows past the block repeat its last row and are masked)
@@ -238,10 +239,10 @@ __device__ inline RowGeom row_geom(const TopCdfArgs& a, int i) {
 // the key block and the sink ranges.
 __device__ inline bool column_forced(const TopCdfArgs& a, int j, float sk) {
     const int64_t k_first = int64_t(j) * a.bk;
-    const int64_t k_end = min(k_first + a.bk, a.N);
+    const int64_t k_end = min(k_first + a.bk, a.Nk);
     bool f = (a.theta > 0.f) && (sk < a.theta);
     f |= (a.sink_front > 0) && (k_first < a.sink_front);
-    f |= (a.sink_back > 0) && (k_end > a.N - a.sink_back);
+    f |= (a.sink_back > 0) && (k_end > a.Nk - a.sink_back);
     return f;
 }
 
@@ -719,10 +720,10 @@ hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_
     auto go = [&](auto gather) {
         constexpr bool G = decltype(gather)::value;
         if (s.D == 128)
-            hipLaunchKernelGGL((k_block_stats<128, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.bq, s.bk, qb,
+            hipLaunchKernelGGL((k_block_stats<128, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
                                qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
         else
-            hipLaunchKernelGGL((k_block_stats<64, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.bq, s.bk, qb,
+            hipLaunchKernelGGL((k_block_stats<64, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
                                qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
     };
     if (perm) go(std::true_type{});

@@ -16,6 +16,7 @@ struct PredictShape {
     int64_t N;
     int bq, bk;
     int64_t n_qb, n_kb;
+    int64_t Nk;    // keys per sequence
     int64_t rows;  // B * Hq * n_qb
     int64_t off[6];
     size_t bytes;
@@ -46,6 +47,7 @@ struct TopCdfArgs {
     int bq, bk;
     int n_qb, n_kb;
     int causal;
+    int64_t Nk;  // keys per sequence (N unless they differ)
     int64_t window, sink_front, sink_back;
     int64_t sink_rows;  // query blocks touching tokens [0, sink_rows) keep their whole valid row
     float tau;       // < 0: unset
@@ -79,6 +81,7 @@ struct FlashArgs {
     int32_t* dev_status;
     int B, Hq, Hkv, D;
     int64_t N;
+    int64_t Nk;  // keys per sequence (N unless they differ)
     int bq, bk;
     int n_qb, n_kb;
     int64_t col_cap;

@@ -40,6 +40,16 @@ class PathConfig:
     sparsity: Optional[float] = None
     lam: Optional[float] = None
     scale: float = 0.0
+    # keys and values on their own latent grid (MindIE-SD latent_shape_k); None = the queries'
+    latent_k: Optional[Tuple[int, int, int]] = None
+    txt_len_k: Optional[int] = None
+
+    @property
+    def N_k(self):
+        if self.latent_k is None and self.txt_len_k is None:
+            return self.N
+        t, h, w = self.latent if self.latent_k is None else self.latent_k
+        return (self.txt_len if self.txt_len_k is None else self.txt_len_k) + t * h * w
 
     @property
     def n_qb(self):
@@ -47,7 +57,7 @@ class PathConfig:
 
     @property
     def n_kb(self):
-        return -(-self.N // self.block_k)
+        return -(-self.N_k // self.block_k)
 
     @property
     def rows(self):
@@ -56,14 +66,23 @@ class PathConfig:
     def mask_params(self):
         return L.make_mask_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
                                   self.causal, self.window_tokens, self.sink_front, self.sink_back,
-                                  self.tau, self.theta, self.sparsity, self.scale, self.sink_rows)
+                                  self.tau, self.theta, self.sparsity, self.scale, self.sink_rows,
+                                  0 if self.N_k == self.N else self.N_k)
 
     def attn_params(self, col_cap=0):
         return L.make_attn_params(self.B, self.Hq, self.Hkv, self.N, self.D, self.block_q, self.block_k,
-                                  self.causal, self.lam, self.scale, col_cap)
+                                  self.causal, self.lam, self.scale, col_cap, 0 if self.N_k == self.N else self.N_k)
 
     def layout(self):
         return L.make_layout(self.N, self.order, self.latent, self.window, self.txt_len, self.first_frame_sink)
+
+    def layout_k(self):
+        """Token layout of the keys and values (the queries' unless latent_k / txt_len_k are set)."""
+        if self.N_k == self.N and self.latent_k is None and self.txt_len_k is None:
+            return self.layout()
+        return L.make_layout(self.N_k, self.order, self.latent if self.latent_k is None else self.latent_k,
+                             self.window, self.txt_len if self.txt_len_k is None else self.txt_len_k,
+                             self.first_frame_sink)
 
 
 def config_from_workload(w, sparsity="default") -> PathConfig:
@@ -73,7 +92,8 @@ def config_from_workload(w, sparsity="default") -> PathConfig:
                       first_frame_sink=w.first_frame_sink, causal=w.causal, window_tokens=w.window_tokens,
                       sink_front=w.sink_front, sink_back=w.sink_back, sink_rows=getattr(w, "sink_rows", 0),
                       tau=w.tau, theta=w.theta,
-                      sparsity=w.sparsity if sparsity == "default" else sparsity, lam=w.lam)
+                      sparsity=w.sparsity if sparsity == "default" else sparsity, lam=w.lam,
+                      latent_k=getattr(w, "latent_k", None), txt_len_k=getattr(w, "txt_len_k", None))
 
 
 class SparseAttentionPath:
@@ -89,12 +109,20 @@ class SparseAttentionPath:
         self.device = device
         self.perm_host = L.sa_plan_permutation(cfg.layout())
         self.perm = torch.from_numpy(self.perm_host).to(device)
+        # keys on their own grid get their own reorder (materialising form only: the gather
+        # entry points take one permutation)
+        self.keys_differ = cfg.N_k != cfg.N or cfg.latent_k is not None or cfg.txt_len_k is not None
+        if self.keys_differ and not materialize:
+            raise ValueError("keys on another latent grid need the materialising form")
+        self.perm_k_host = L.sa_plan_permutation(cfg.layout_k()) if self.keys_differ else self.perm_host
+        self.perm_k = torch.from_numpy(self.perm_k_host).to(device) if self.keys_differ else self.perm
         bf = torch.bfloat16
         B, Hq, Hkv, N, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.D
+        Nk = cfg.N_k
         # reordered copies (only for the materialising form)
         self.qp = torch.empty((B, Hq, N, D), dtype=bf, device=device) if materialize else None
-        self.kp = torch.empty((B, Hkv, N, D), dtype=bf, device=device) if materialize else None
-        self.vp = torch.empty((B, Hkv, N, D), dtype=bf, device=device) if materialize else None
+        self.kp = torch.empty((B, Hkv, Nk, D), dtype=bf, device=device) if materialize else None
+        self.vp = torch.empty((B, Hkv, Nk, D), dtype=bf, device=device) if materialize else None
         self.mp = cfg.mask_params()
         ws_bytes = L.sa_predict_workspace_bytes(self.mp)
         if ws_bytes == 0:
@@ -122,8 +150,8 @@ class SparseAttentionPath:
     # --- the four steps (each one C-ABI call, or three for the permute) ---
     def permute(self, q, k, v, stream=None):
         L.sa_permute(q, self.qp, self.perm, stream)
-        L.sa_permute(k, self.kp, self.perm, stream)
-        L.sa_permute(v, self.vp, self.perm, stream)
+        L.sa_permute(k, self.kp, self.perm_k, stream)
+        L.sa_permute(v, self.vp, self.perm_k, stream)
 
     def _cols(self):
         return self.col_idx[:self.col_cap] if self.col_cap > 0 else self.col_idx[:0]

@@ -100,7 +100,10 @@ typedef struct sa_mask_params {
     double theta;             /* self-similarity guard; <= 0 = off */
     double sparsity;          /* keep floor: ceil((1-s)*|valid|) blocks per row, s in [0,1); negative = unset */
     float scale;              /* score scale; 0 = 1/sqrt(D) */
-    int32_t reserved1;        /* must be 0 */
+    int32_t n_keys;           /* keys per sequence when they differ from the N queries
+                                 (MindIE-SD latent_shape_k != latent_shape_q); 0 = N;
+                                 not with causal; k is then [B,Hkv,n_keys,D] and the key
+                                 blocks, back sink and key similarity cover n_keys tokens */
 } sa_mask_params;
 
 /* Sparse attention parameters (SpargeAttn notes, section 2.1 table). */
@@ -113,6 +116,7 @@ typedef struct sa_attn_params {
     float lambda;             /* PV-skip threshold (< 0); -INFINITY = off */
     float scale;              /* 0 = 1/sqrt(D) */
     int64_t col_cap;          /* entries col_idx holds; CSR entries at or past it are not read */
+    int64_t n_keys;           /* keys per sequence, k and v [B,Hkv,n_keys,D]; 0 = N; not with causal */
 } sa_attn_params;
 
 /* Static text for a status code.  Never NULL. */
@@ -226,8 +230,8 @@ int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* 
  * with pv_skip[e*G + g] = 1 when group g skipped the PV of CSR entry e;
  * counters device int64 [3] = {QK block products, PV group-blocks executed,
  * PV group-blocks skipped}, reset by the call.
- * N * D * 2 must be below 2^31 (one head of k or v under 2 GiB), else
- * SA_ERR_UNSUPPORTED. */
+ * max(N, n_keys) * D * 2 must be below 2^31 (one head of q, k or v under
+ * 2 GiB), else SA_ERR_UNSUPPORTED. */
 int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
                        const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
                        uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream);
@@ -246,6 +250,8 @@ int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
  * perm_dev must be a permutation of 0..N-1.  This is not checked; an entry
  * outside 0..N-1 never makes a kernel access memory outside q, k, v and o,
  * but the results are then unspecified.
+ * One permutation serves queries and keys, so n_keys must be 0 or N (keys of
+ * another length: SA_ERR_UNSUPPORTED; reorder them with sa_permute instead).
  * Other arguments, errors and outputs as in the non-gather calls; perm_dev must
  * not be NULL. */
 int sa_predict_mask_gather(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
@@ -258,7 +264,8 @@ int sa_sparse_attn_fwd_gather(const uint16_t* q, const uint16_t* k, const uint16
                               int64_t* counters, int32_t* dev_status, void* stream);
 
 /* sa_predict_mask with both options in one call: perm_dev as in
- * sa_predict_mask_gather (NULL: q and k are already in the reordered order),
+ * sa_predict_mask_gather (NULL: q and k are already in the reordered order;
+ * non-NULL only with n_keys 0 or N, else SA_ERR_UNSUPPORTED),
  * and forced_dev, a device uint8 [n_qb*n_kb] block pattern shared by every
  * (batch, head) (NULL: none), e.g. the tile windows of sa_plan_tile_window:
  * a nonzero entry (i, j) adds key block j to the forced blocks of query

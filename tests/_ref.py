@@ -28,6 +28,14 @@ def oracle_perm(w) -> np.ndarray:
     return OL.plan_permutation(w.N, w.order, w.latent, w.window, w.txt_len, w.first_frame_sink)
 
 
+def oracle_perm_k(w) -> np.ndarray:
+    """The keys' reorder: their own grid when the workload gives one."""
+    if w.latent_k is None and w.txt_len_k is None:
+        return oracle_perm(w)
+    return OL.plan_permutation(w.N_k, w.order, w.latent if w.latent_k is None else w.latent_k, w.window,
+                               w.txt_len if w.txt_len_k is None else w.txt_len_k, w.first_frame_sink)
+
+
 def permuted(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
     return OL.permute_rows(to_f64(x), perm)
 
@@ -42,7 +50,8 @@ def tile_pattern(w):
 
 def mask_params(w, sparsity="default") -> OP.MaskParams:
     s = w.sparsity if sparsity == "default" else sparsity
-    return OP.MaskParams(N=w.N, block_q=w.block_q, block_k=w.block_k, causal=w.causal, forced=tile_pattern(w),
+    return OP.MaskParams(N=w.N, N_k=None if w.N_k == w.N else w.N_k, block_q=w.block_q, block_k=w.block_k,
+                         causal=w.causal, forced=tile_pattern(w),
                          window=w.window_tokens, sink_front=w.sink_front, sink_back=w.sink_back,
                          sink_rows=w.sink_rows,
                          tau=w.tau, theta=w.theta, sparsity=s)

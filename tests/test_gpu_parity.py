@@ -48,6 +48,19 @@ SMALL = {
     # 3-D tile windows ([4,8,4] tiles, one tile of reach) forced on top of the prediction
     "video_s_tiles": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20,
                          sink_front=16 * 24, sink_back=20, tile=(4, 8, 4), tile_radius=(1, 1, 1), seed=93),
+    # keys and values on a grid of their own (half the width; the first key frame and the key
+    # text are the sinks), one case per attention kernel: 16-blocks, 128-key blocks with and
+    # without PV skip, 64-key blocks with PV skip, and d = 64
+    "tiny_kv": rep(CONFIGS["tiny"], latent_k=(2, 4, 4), seed=101),
+    "video_s_kv": rep(CONFIGS["video"], Hq=2, Hkv=2, latent=(9, 16, 24), txt_len=20, latent_k=(9, 16, 12),
+                      sink_front=16 * 12, sink_back=20, seed=103),
+    "image_s_lam_kv": rep(CONFIGS["image"], Hq=3, Hkv=3, latent=(1, 20, 37), latent_k=(1, 10, 19), lam=-8.0,
+                          seed=105),
+    # (theta off: at this size every block falls under the 0.6 guard and the rows would be full)
+    "long_video_s_kv": rep(CONFIGS["long_video"], Hq=2, Hkv=2, latent=(6, 10, 21), latent_k=(3, 10, 21),
+                           theta=None, seed=107),
+    "long_video_d64_kv": rep(CONFIGS["long_video"], Hq=2, Hkv=2, latent=(5, 9, 23), latent_k=(5, 9, 12), D=64,
+                             theta=None, lam=None, seed=109),
 }
 
 
@@ -93,23 +106,28 @@ def run_path(w, sparsity="default"):
 @pytest.mark.parametrize("name", list(SMALL))
 def test_path_parity(name):
     w = SMALL[name]
-    log(f"[parity] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k}")
+    log(f"[parity] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} N_k={w.N_k} D={w.D} bq={w.block_q} bk={w.block_k}")
     path, (q, k, v), gmask, gsimq, gsimk = run_path(w)
     cfg = path.cfg
     st_pred, st_attn = path.statuses()
     assert st_pred == sa.SA_OK and st_attn == sa.SA_OK
 
-    # (a1) permutation: planner and gathered rows, bit-exact
+    # (a1) permutation: planner and gathered rows, bit-exact (keys on their own grid have
+    # their own reorder)
     perm = R.oracle_perm(w)
+    perm_k = R.oracle_perm_k(w)
     assert np.array_equal(path.perm_host.astype(np.int64), perm)
+    assert np.array_equal(path.perm_k_host.astype(np.int64), perm_k)
     want_q = ON.f32_to_bf16(q) if q.dtype == np.float32 else q
     assert np.array_equal(host_bits(path.qp), np.take(want_q, perm, axis=2))
+    want_k = ON.f32_to_bf16(k) if k.dtype == np.float32 else k
+    assert np.array_equal(host_bits(path.kp), np.take(want_k, perm_k, axis=2))
     want_v = ON.f32_to_bf16(v) if v.dtype == np.float32 else v
-    assert np.array_equal(host_bits(path.vp), np.take(want_v, perm, axis=2))
+    assert np.array_equal(host_bits(path.vp), np.take(want_v, perm_k, axis=2))
 
     qp = R.permuted(q, perm)
-    kp = R.permuted(k, perm)
-    vp = R.permuted(v, perm)
+    kp = R.permuted(k, perm_k)
+    vp = R.permuted(v, perm_k)
     G = w.Hq // w.Hkv
     mp = R.mask_params(w)
     qbar_g = path.workspace_view(0, torch.float32, (cfg.B, cfg.Hq, cfg.n_qb, cfg.D)).cpu().numpy()
@@ -349,6 +367,12 @@ def test_gather_form_bit_identical(name):
     w = SMALL[name]
     cfg = sa.config_from_workload(w)
     log(f"[gather] {name}: N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam} causal={w.causal}")
+    if w.N_k != w.N:
+        # one permutation serves queries and keys in the gather form: keys on another grid
+        # are refused before anything runs
+        with pytest.raises(ValueError):
+            sa.SparseAttentionPath(cfg, materialize=False)
+        return
     qd, kd, vd = _bf16_inputs(w)
     a, b = run_both_forms(cfg, qd, kd, vd, forced=library_tile_pattern(w))
     assert a["status"] == (sa.SA_OK, sa.SA_OK)

@@ -182,6 +182,53 @@ def test_predict_ex_validates_like_predict():
     assert code(good, ws=None) == sa.SA_ERR_INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_keys=-1), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(n_keys=500, causal=True), sa.SA_ERR_INVALID_ARGUMENT),   # a causal mask needs N_k = N
+    (dict(n_keys=300, sink_front=301), sa.SA_ERR_INVALID_ARGUMENT),  # sinks count keys
+    (dict(n_keys=300, sink_back=301), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(n_keys=sa.SA_MAX_KEY_BLOCKS * 64 + 1, block_k=64), sa.SA_ERR_UNSUPPORTED),
+])
+def test_predict_rejects_bad_key_lengths(kw, code):
+    p = _mask_params(**kw)
+    assert sa.sa_predict_workspace_bytes(p) == 0
+    assert _predict_code(p) == code
+
+
+def test_key_length_sizes_the_key_side_of_the_workspace():
+    """kbar and simk follow the keys' block count, everything else the queries'."""
+    p = _mask_params(B=2, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64, n_keys=300,
+                     sink_front=300, sink_back=300)
+    off = sa.sa_predict_workspace_offsets(p)
+    n_qb, n_kb = 8, 5
+    sizes = [2 * 4 * n_qb * 128 * 4, 2 * 2 * n_kb * 128 * 4, 2 * 4 * n_qb * 4, 2 * 2 * n_kb * 4,
+             2 * 4 * n_qb * n_kb, 2 * 4 * n_qb * 4]
+    for i in range(6):
+        end = off[i] + sizes[i]
+        nxt = off[i + 1] if i < 5 else sa.sa_predict_workspace_bytes(p)
+        assert end <= nxt
+    # n_keys = N is the same call as n_keys = 0
+    assert sa.sa_predict_workspace_bytes(_mask_params(n_keys=1000)) == sa.sa_predict_workspace_bytes(_mask_params())
+
+
+def test_gather_forms_reject_keys_of_another_length():
+    """The gather entry points take one permutation for queries and keys."""
+    assert _predict_gather_code(_mask_params(n_keys=300)) == sa.SA_ERR_UNSUPPORTED
+    assert _attn_gather_code(sa.make_attn_params(1, 4, 2, 1000, 128, 128, 64, n_keys=300)) == sa.SA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_keys=-1), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(n_keys=1 << 31), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(n_keys=500, causal=True), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(n_keys=(1 << 30) // 128), sa.SA_ERR_UNSUPPORTED),  # a key head of 2 GiB
+])
+def test_attn_rejects_bad_key_lengths(kw, code):
+    base = dict(B=1, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64)
+    base.update(kw)
+    assert _attn_code(sa.make_attn_params(**base)) == code
+
+
 def test_predict_accepts_the_largest_key_block_count():
     p = _mask_params(N=sa.SA_MAX_KEY_BLOCKS * 64, block_k=64)
     assert sa.sa_predict_workspace_bytes(p) > 0

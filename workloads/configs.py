@@ -53,6 +53,8 @@ class Workload:
     sink_rows: int = 0            # tokens at the front whose query blocks keep their whole row
     tile: Optional[Tuple[int, int, int]] = None  # 3-D tile windows forced as blocks (None = off)
     tile_radius: Tuple[int, int, int] = (0, 0, 0)  # their reach in tiles along t, h, w
+    latent_k: Optional[Tuple[int, int, int]] = None  # keys/values on their own grid (None: the latent)
+    txt_len_k: Optional[int] = None               # text tokens among the keys (None: txt_len)
     tau: Optional[float] = None   # TopCdf cumulative mass (None = unset)
     theta: Optional[float] = None  # self-similarity guard (None = off)
     sparsity: Optional[float] = None  # keep floor (None = unset)
@@ -64,6 +66,11 @@ class Workload:
     def N(self) -> int:
         t, h, w = self.latent
         return self.txt_len + t * h * w
+
+    @property
+    def N_k(self) -> int:
+        t, h, w = self.latent if self.latent_k is None else self.latent_k
+        return (self.txt_len if self.txt_len_k is None else self.txt_len_k) + t * h * w
 
     def with_sparsity(self, s: Optional[float]) -> "Workload":
         return replace(self, sparsity=s)

@@ -12,7 +12,9 @@ Recipes (the same ones the design doc lists):
   phi ~ U(0, 2*pi), amplitude 1 each.  Q = F + 0.3*N(0,1), K = F + 0.3*N(0,1)
   (shared field, independent noise); 1% of tokens (Bernoulli per token,
   independent for Q and K) are scaled by 8.  Text tokens, when present, are
-  iid N(0,1) and are prepended.  V ~ N(0,1).
+  iid N(0,1) and are prepended.  V ~ N(0,1).  Keys on a grid of their own
+  (``latent_k``) sample the same field (same draws) at that grid's normalised
+  coordinates, with ``txt_len_k`` text tokens; V then has the keys' length.
 * causal_long: per KV head an orthonormal U (128x16, QR of a Gaussian) and a
   drift z_r(t) = 2 sin(2*pi*f_r*t/N + phi_r), f_r ~ U(0.5, 4); Q and K of every
   head in the group are N(0,1) + U z(t); the keys at positions 0..3 are
@@ -42,15 +44,23 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def _smooth_field(rng: np.random.Generator, latent, C: int) -> np.ndarray:
-    """Sum of _NSIN sinusoids per channel over a (T,H,W) grid -> float32 [T*H*W, C].
+def _field_draws(rng: np.random.Generator, C: int):
+    """Frequencies U(0,1)^3 and phases U(0, 2*pi) of the _NSIN sinusoids of each channel."""
+    freq = rng.uniform(0.0, 1.0, size=(C, _NSIN, 3))
+    phase = rng.uniform(0.0, 2.0 * np.pi, size=(C, _NSIN))
+    return freq, phase
 
+
+def _eval_field(freq: np.ndarray, phase: np.ndarray, latent) -> np.ndarray:
+    """Sum of the sinusoids over a (T,H,W) grid -> float32 [T*H*W, C].
+
+    Coordinates are normalised (t/T, h/H, w/W), so one set of draws evaluated
+    on two grids gives the same field sampled at two resolutions.
     sin(a+b+c) is expanded into four products so the whole grid is one batched
     matrix product per channel instead of T*H*W*_NSIN sine evaluations.
     """
     T, H, W = latent
-    freq = rng.uniform(0.0, 1.0, size=(C, _NSIN, 3))
-    phase = rng.uniform(0.0, 2.0 * np.pi, size=(C, _NSIN))
+    C = freq.shape[0]
     two_pi = 2.0 * np.pi
     a = two_pi * freq[:, :, 0:1] * (np.arange(T) / T)[None, None, :] + phase[:, :, None]
     b = two_pi * freq[:, :, 1:2] * (np.arange(H) / H)[None, None, :]
@@ -73,22 +83,25 @@ def _outliers(rng: np.random.Generator, x: np.ndarray) -> None:
 
 def _gen_field(cfg: Workload):
     rng = np.random.default_rng(cfg.seed)
-    B, H, D, N = cfg.B, cfg.Hq, cfg.D, cfg.N
+    B, H, D, N, Nk = cfg.B, cfg.Hq, cfg.D, cfg.N, cfg.N_k
     assert cfg.Hq == cfg.Hkv
+    txt_k = cfg.txt_len if cfg.txt_len_k is None else cfg.txt_len_k
     q = np.empty((B, H, N, D), dtype=np.uint16)
-    k = np.empty((B, H, N, D), dtype=np.uint16)
-    nv = N - cfg.txt_len
+    k = np.empty((B, H, Nk, D), dtype=np.uint16)
     for b in range(B):
         for h in range(H):
-            F = _smooth_field(rng, cfg.latent, D)
-            for dst in (q, k):
-                x = np.empty((N, D), dtype=np.float32)
-                x[cfg.txt_len:] = F + _NOISE * rng.standard_normal((nv, D), dtype=np.float32)
-                if cfg.txt_len:
-                    x[:cfg.txt_len] = rng.standard_normal((cfg.txt_len, D), dtype=np.float32)
+            freq, phase = _field_draws(rng, D)
+            F = _eval_field(freq, phase, cfg.latent)
+            Fk = F if cfg.latent_k is None else _eval_field(freq, phase, cfg.latent_k)
+            for dst, field, txt in ((q, F, cfg.txt_len), (k, Fk, txt_k)):
+                n = txt + field.shape[0]
+                x = np.empty((n, D), dtype=np.float32)
+                x[txt:] = field + _NOISE * rng.standard_normal((n - txt, D), dtype=np.float32)
+                if txt:
+                    x[:txt] = rng.standard_normal((txt, D), dtype=np.float32)
                 _outliers(rng, x)
                 dst[b, h] = bf16_bits(x)
-    v = bf16_bits(rng.standard_normal((B, H, N, D), dtype=np.float32))
+    v = bf16_bits(rng.standard_normal((B, H, Nk, D), dtype=np.float32))
     return q, k, v
 
 
@@ -121,7 +134,7 @@ def _gen_causal(cfg: Workload):
 def _gen_iid_f32(cfg: Workload):
     rng = np.random.default_rng(cfg.seed)
     shape_q = (cfg.B, cfg.Hq, cfg.N, cfg.D)
-    shape_kv = (cfg.B, cfg.Hkv, cfg.N, cfg.D)
+    shape_kv = (cfg.B, cfg.Hkv, cfg.N_k, cfg.D)
     q = rng.standard_normal(shape_q).astype(np.float32)
     k = rng.standard_normal(shape_kv).astype(np.float32)
     v = rng.standard_normal(shape_kv).astype(np.float32)
