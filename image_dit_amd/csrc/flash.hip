@@ -954,6 +954,9 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             const uint16_t* K = Ks[kbuf];
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+            // the score products issue ahead of the other wave of this SIMD, whose
+            // softmax then fills the VALU while the matrix core runs
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
@@ -962,6 +965,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
             if ((kb0 + BK > Nk) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
