@@ -32,7 +32,11 @@ pytestmark = [pytest.mark.gpu,
 FULL_W = {name: CONFIGS[name] for name in ["image", "video", "long_video", "causal_long"]}
 FULL_W["max_blocks_lam"] = dataclasses.replace(CONFIGS["long_video"], Hq=1, Hkv=1, latent=(2, 256, 256), seed=81)
 FULL_W["max_blocks_causal"] = dataclasses.replace(CONFIGS["causal_long"], Hq=2, Hkv=1, block_k=64, seed=82)
+# the video workload with keys and values on a grid of half its width (12514 keys for 24802
+# queries; the first key frame and the key text are the sinks); materialising form only
+FULL_W["video_kv"] = dataclasses.replace(CONFIGS["video"], latent_k=(16, 32, 24), sink_front=32 * 24, seed=83)
 FULL = list(FULL_W)
+FULL_GATHER = [name for name in FULL if FULL_W[name].N_k == FULL_W[name].N]
 
 
 def log(*a):
@@ -47,7 +51,7 @@ def dev(x):
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_parity(name):
     w = FULL_W[name]
-    log(f"[full] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bq={w.block_q} bk={w.block_k}")
+    log(f"[full] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} N_k={w.N_k} D={w.D} bq={w.block_q} bk={w.block_k}")
     q, k, v = generate(w)
     cfg = sa.config_from_workload(w)
     path = sa.SparseAttentionPath(cfg)
@@ -63,13 +67,15 @@ def test_full_size_sampled_parity(name):
 
     rng = np.random.default_rng(12345)
     perm = R.oracle_perm(w)
+    perm_k = R.oracle_perm_k(w)
     assert np.array_equal(path.perm_host.astype(np.int64), perm)
+    assert np.array_equal(path.perm_k_host.astype(np.int64), perm_k)
     # sampled permuted rows, bit-exact
-    for src, dst, H in ((q, path.qp, w.Hq), (k, path.kp, w.Hkv), (v, path.vp, w.Hkv)):
-        bs, hs, ts = rng.integers(0, w.B, 64), rng.integers(0, H, 64), rng.integers(0, w.N, 64)
+    for src, dst, H, pm in ((q, path.qp, w.Hq, perm), (k, path.kp, w.Hkv, perm_k), (v, path.vp, w.Hkv, perm_k)):
+        bs, hs, ts = rng.integers(0, w.B, 64), rng.integers(0, H, 64), rng.integers(0, len(pm), 64)
         got = dst[torch.from_numpy(bs).cuda(), torch.from_numpy(hs).cuda(), torch.from_numpy(ts).cuda()]
         got = got.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert np.array_equal(got, src[bs, hs, perm[ts]])
+        assert np.array_equal(got, src[bs, hs, pm[ts]])
 
     gmask = mask.cpu().numpy().astype(bool)
     rp, ci = path.csr_host()
@@ -97,8 +103,8 @@ def test_full_size_sampled_parity(name):
     for b, h in heads:
         hk = h // G
         qp = R.permuted(q[b, h], perm)
-        kp = R.permuted(k[b, hk], perm)
-        vp = R.permuted(v[b, hk], perm)
+        kp = R.permuted(k[b, hk], perm_k)
+        vp = R.permuted(v[b, hk], perm_k)
         rows = sorted(set(np.linspace(0, cfg.n_qb - 1, 24).astype(int).tolist()))
         ref = OP.predict_head(qp, kp, mp, rows=rows)
         r0 = (b * w.Hq + h) * cfg.n_qb
@@ -130,7 +136,7 @@ def test_full_size_sampled_parity(name):
     assert worst_max <= R.MAX_ABS and sum_abs / n_el <= R.MEAN_ABS
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL_GATHER)
 def test_full_size_gather_form_bit_identical(name):
     """At full size, the gather form (the one the benchmark times) equals the
     materialising form bit for bit: CSR, mask, statistics, skip flags,
