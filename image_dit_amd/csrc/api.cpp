@@ -40,6 +40,8 @@ int validate_predict(const sa_mask_params* p) {
     if (!head_dim_ok(p->D)) return SA_ERR_UNSUPPORTED;
     const int64_t n_kb = (nk + p->block_k - 1) / p->block_k;
     if (n_kb > SA_MAX_KEY_BLOCKS) return SA_ERR_UNSUPPORTED;
+    // row_ptr entries are int32
+    if (int64_t(p->B) * p->Hq * ((p->N + p->block_q - 1) / p->block_q) + 1 > INT32_MAX) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
 
@@ -88,6 +90,9 @@ int validate_attn(const sa_attn_params* p) {
     const bool pair_ok = (p->block_q == 16 && p->block_k == 16) ||
                          (p->block_q == 128 && (p->block_k == 64 || p->block_k == 128));
     if (!pair_ok) return SA_ERR_UNSUPPORTED;
+    // rows (one workgroup each) and row_ptr entries are int32
+    const int64_t rows = int64_t(p->B) * p->Hq * ((p->N + p->block_q - 1) / p->block_q);
+    if (rows + 1 > INT32_MAX) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
 
@@ -113,6 +118,7 @@ extern "C" int sa_permute(const void* x, int x_dtype, uint16_t* y, const int32_t
         return SA_ERR_INVALID_ARGUMENT;
     if (x_dtype != SA_BF16 && x_dtype != SA_F32) return SA_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) return SA_ERR_INVALID_ARGUMENT;
+    if (N * (D / 8) > INT32_MAX) return SA_ERR_UNSUPPORTED;  // one (row, chunk) index per thread, int32
     const hipError_t e = launch_permute(x, x_dtype, y, perm, int64_t(B) * H, N, D,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
@@ -123,6 +129,7 @@ extern "C" int sa_unpermute(const float* y, float* x, const int32_t* perm, int32
     if (!x || !y || !perm || B <= 0 || H <= 0 || N <= 0 || N > INT32_MAX || Dv <= 0 || Dv % 4 != 0)
         return SA_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) return SA_ERR_INVALID_ARGUMENT;
+    if (N * (Dv / 4) > INT32_MAX) return SA_ERR_UNSUPPORTED;  // one (row, chunk) index per thread, int32
     const hipError_t e = launch_unpermute(y, x, perm, int64_t(B) * H, N, Dv,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
@@ -156,7 +163,6 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
         return SA_ERR_INVALID_ARGUMENT;
     if (ws_bytes < s.bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return SA_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15) return SA_ERR_INVALID_ARGUMENT;
-    if (s.rows + 1 > INT32_MAX) return SA_ERR_UNSUPPORTED;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);

@@ -29,10 +29,12 @@ __global__ __launch_bounds__(256) void k_permute(const void* __restrict__ x, uin
     const int c = t - i * chunks;
     const int src = perm[i];
     const int64_t D = int64_t(chunks) * 8;
+    const bool ok = uint32_t(src) < uint32_t(N);  // an entry outside 0..N-1 reads nothing and writes zeros
     for (int64_t bh = blockIdx.y; bh < bh_count; bh += gridDim.y) {
         const int64_t base = bh * N;
-        uint4 out;
-        if constexpr (kF32) {
+        uint4 out = make_uint4(0, 0, 0, 0);
+        if (!ok) {
+        } else if constexpr (kF32) {
             const f32x4* xs = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + (base + src) * D) + 2 * c;
             const f32x4 a = __builtin_nontemporal_load(xs);
             const f32x4 b = __builtin_nontemporal_load(xs + 1);
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void k_unpermute(const float* __restrict__ y, 
     const int i = t / chunks;
     const int c = t - i * chunks;
     const int dst = perm[i];
+    if (uint32_t(dst) >= uint32_t(N)) return;  // an entry outside 0..N-1 stores nothing
     const int64_t D = int64_t(chunks) * 4;
     for (int64_t bh = blockIdx.y; bh < bh_count; bh += gridDim.y) {
         const int64_t base = bh * N;

@@ -152,8 +152,10 @@ int sa_plan_tile_window(const sa_layout* L, int32_t tile_t, int32_t tile_h, int3
 /* Row gather with conversion to bf16 (SparseAttn article, section 3.4):
  *   y[b,h,i,:] = bf16_round_nearest_even(x[b,h,perm[i],:])
  * x: device [B,H,N,D] of x_dtype (SA_BF16 or SA_F32); y: device bf16 [B,H,N,D];
- * perm_dev: device int32 [N], a permutation of 0..N-1 (not checked).
- * D must be a multiple of 8.  With the identity permutation this is the
+ * perm_dev: device int32 [N], a permutation of 0..N-1 (not checked; a row
+ * whose entry lies outside 0..N-1 reads nothing and is written as zeros).
+ * D must be a multiple of 8 and N * D/8 must fit in int32 (else
+ * SA_ERR_UNSUPPORTED).  With the identity permutation this is the
  * documented way to hand fp32 inputs to the bf16 kernels.  x and y must not
  * overlap. */
 int sa_permute(const void* x, int x_dtype, uint16_t* y, const int32_t* perm_dev,
@@ -161,7 +163,10 @@ int sa_permute(const void* x, int x_dtype, uint16_t* y, const int32_t* perm_dev,
 
 /* Inverse row scatter (SparseAttn article, section 3.4):
  *   x[b,h,perm[i],:] = y[b,h,i,:]
- * y, x: device fp32 [B,H,N,Dv] (no overlap); perm_dev: device int32 [N]. */
+ * y, x: device fp32 [B,H,N,Dv] (no overlap); perm_dev: device int32 [N], a
+ * permutation of 0..N-1 (not checked; an entry outside 0..N-1 stores nothing).
+ * Dv must be a multiple of 4 and N * Dv/4 must fit in int32 (else
+ * SA_ERR_UNSUPPORTED). */
 int sa_unpermute(const float* y, float* x, const int32_t* perm_dev,
                  int32_t B, int32_t H, int64_t N, int32_t Dv, void* stream);
 
@@ -181,9 +186,9 @@ size_t sa_predict_workspace_bytes(const sa_mask_params* p);
 int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
 
 /* Block-mask prediction on the PERMUTED q (device bf16 [B,Hq,N,D]) and k
- * (device bf16 [B,Hkv,N,D]) (SpargeAttn notes, section 2.2; MindIE-SD rf_v2).
- * Per (batch b, query head h, query block i), with n_qb = ceil(N/b_q),
- * n_kb = ceil(N/b_k), KV head h / (Hq/Hkv):
+ * (device bf16 [B,Hkv,N_k,D], N_k = n_keys or N) (SpargeAttn notes, section 2.2;
+ * MindIE-SD rf_v2).  Per (batch b, query head h, query block i), with
+ * n_qb = ceil(N/b_q), n_kb = ceil(N_k/b_k), KV head h / (Hq/Hkv):
  *   1. block means and similarity ||mean_t x_t/||x_t||||^2 over the block's real tokens;
  *   2. valid key blocks: all, or (causal) those whose first token is not after
  *      the query block's last token;
@@ -205,7 +210,8 @@ int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
  * the full count).  Optional (NULL = not written): mask_out device uint8
  * [B,Hq,n_qb,n_kb] (1 = kept), sim_q device fp32 [B,Hq,n_qb], sim_k device fp32
  * [B,Hkv,n_kb].  ws: device workspace of ws_bytes >= sa_predict_workspace_bytes(p),
- * 256-byte aligned.  n_kb must not exceed SA_MAX_KEY_BLOCKS. */
+ * 256-byte aligned.  n_kb must not exceed SA_MAX_KEY_BLOCKS and B*Hq*n_qb + 1
+ * must fit in int32 (else SA_ERR_UNSUPPORTED). */
 int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* p,
                     void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                     int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
@@ -231,7 +237,8 @@ int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* 
  * counters device int64 [3] = {QK block products, PV group-blocks executed,
  * PV group-blocks skipped}, reset by the call.
  * max(N, n_keys) * D * 2 must be below 2^31 (one head of q, k or v under
- * 2 GiB), else SA_ERR_UNSUPPORTED. */
+ * 2 GiB) and B*Hq*ceil(N/block_q) + 1 must fit in int32, else
+ * SA_ERR_UNSUPPORTED. */
 int sa_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
                        const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
                        uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream);

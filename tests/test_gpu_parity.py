@@ -248,6 +248,32 @@ def test_permute_fp32_round_to_nearest_even():
     assert np.array_equal(back.cpu().numpy(), OL.unpermute_rows(ON.bf16_to_f64(want).astype(np.float32), perm))
 
 
+def test_permute_entries_outside_the_sequence():
+    """Entries outside 0..N-1 are caught by the kernels' own bounds checks: the gather
+    writes a zero row, the scatter stores nothing."""
+    rng = np.random.default_rng(5)
+    N, D = 100, 16
+    x = rng.normal(size=(1, 2, N, D)).astype(np.float32)
+    perm = np.arange(N, dtype=np.int32)
+    perm[5], perm[7] = N, -1
+    y = torch.empty((1, 2, N, D), dtype=torch.bfloat16, device="cuda")
+    sa.sa_permute(dev(x), y, torch.from_numpy(perm).cuda())
+    torch.cuda.synchronize()
+    got = host_bits(y)
+    want = ON.f32_to_bf16(x)
+    ok = np.ones(N, dtype=bool)
+    ok[[5, 7]] = False
+    assert np.array_equal(got[:, :, ok], want[:, :, ok])
+    assert not got[:, :, ~ok].any()
+    yf = dev(x)
+    back = torch.full((1, 2, N, D), 7.0, dtype=torch.float32, device="cuda")
+    sa.sa_unpermute(yf, back, torch.from_numpy(perm).cuda())
+    torch.cuda.synchronize()
+    b = back.cpu().numpy()
+    assert np.array_equal(b[:, :, ok], x[:, :, ok])
+    assert np.all(b[:, :, ~ok] == 7.0)  # rows 5 and 7 are nobody's target
+
+
 def test_empty_row_gives_nan_and_status():
     w = rep(SMALL["long_video_s"], lam=None)
     cfg = sa.config_from_workload(w)

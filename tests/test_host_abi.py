@@ -319,6 +319,20 @@ def test_attn_rejects_heads_of_2gib():
     assert _attn_code(sa.make_attn_params(1, 1, 1, (1 << 30) // 64, 64, 128, 64)) == sa.SA_ERR_UNSUPPORTED
 
 
+def test_attn_rejects_more_rows_than_int32():
+    # B * Hq * n_qb query-block rows, one workgroup and one row_ptr entry each
+    assert _attn_code(sa.make_attn_params(1 << 12, 1 << 12, 1 << 12, 128 * 128, 128, 128, 64)) == \
+        sa.SA_ERR_UNSUPPORTED
+    assert _attn_code(sa.make_attn_params(1 << 10, 1 << 10, 1 << 10, 128 * 128, 128, 128, 64, col_cap=-1)) == \
+        sa.SA_ERR_INVALID_ARGUMENT
+
+
+def test_predict_rejects_more_rows_than_int32():
+    p = _mask_params(B=1 << 12, Hq=1 << 12, Hkv=1 << 12, N=128 * 128, block_q=128, block_k=128)
+    assert sa.sa_predict_workspace_bytes(p) == 0
+    assert _predict_code(p) == sa.SA_ERR_UNSUPPORTED
+
+
 def test_attn_rejects_bad_buffers():
     p = sa.make_attn_params(1, 4, 2, 1000, 128, 128, 64)
     assert _attn_code(p, v=None) == sa.SA_ERR_INVALID_ARGUMENT
@@ -331,3 +345,6 @@ def test_permute_rejects_invalid_arguments():
     assert L.sa_permute(FAKE, 7, FAKE, FAKE, 1, 1, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
     assert L.sa_permute(None, sa.SA_BF16, FAKE, FAKE, 1, 1, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
     assert L.sa_unpermute(FAKE, FAKE, FAKE, 1, 0, 10, 16, None) == sa.SA_ERR_INVALID_ARGUMENT
+    # one int32 (row, chunk) index per thread
+    assert L.sa_permute(FAKE, sa.SA_BF16, FAKE, FAKE, 1, 1, 1 << 26, 256, None) == sa.SA_ERR_UNSUPPORTED
+    assert L.sa_unpermute(FAKE, FAKE, FAKE, 1, 1, 1 << 26, 128, None) == sa.SA_ERR_UNSUPPORTED
