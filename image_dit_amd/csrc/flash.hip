@@ -133,11 +133,15 @@ __global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
     const float lam2 = a.lambda * kLog2e;
     int n_exec = 0, n_skip = 0;
 
-    const int e0 = a.row_ptr[row];
+    int e0 = a.row_ptr[row];
     int e1 = a.row_ptr[row + 1];
     if (e1 > a.col_cap) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
+    }
+    if (e0 < 0) {  // a malformed row_ptr: the row reads no entry
+        if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+        e0 = e1 = 0;
     }
     for (int e = e0; e < e1; ++e) {
         const int jblk = a.col_idx[e];
@@ -485,11 +489,15 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qsrc * D + ks * 16 + half * 8) * 2u));
     }
 
-    const int e0 = row_ptr[row];
+    int e0 = row_ptr[row];
     int e1 = row_ptr[row + 1];
     if (e1 > a.col_cap) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
+    }
+    if (e0 < 0) {  // a malformed row_ptr: the row reads no entry
+        if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+        e0 = e1 = 0;
     }
     const int nt = (e1 > e0 ? e1 - e0 : 0) * SUB;
 
@@ -781,11 +789,15 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             qf[ks] = as_bf16x8(bload16(rQ, uint32_t(qsrc * D + ks * 16 + half * 8) * 2u));
     }
 
-    const int e0 = row_ptr[row];
+    int e0 = row_ptr[row];
     int e1 = row_ptr[row + 1];
     if (e1 > a.col_cap) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
+    }
+    if (e0 < 0) {  // a malformed row_ptr: the row reads no entry
+        if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+        e0 = e1 = 0;
     }
     const int nt = e1 > e0 ? e1 - e0 : 0;
 
@@ -1117,11 +1129,15 @@ __global__ __launch_bounds__(256) void k_flash_small(FlashArgs a) {
     for (int u = 0; u < D / B; ++u) O[u] = 0.f;
     const bool lam_on = a.lambda > -INFINITY;
     int n_exec = 0, n_skip = 0;
-    const int e0 = a.row_ptr[row];
+    int e0 = a.row_ptr[row];
     int e1 = a.row_ptr[row + 1];
     if (e1 > a.col_cap) {
         if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
         e1 = int(a.col_cap);
+    }
+    if (e0 < 0) {  // a malformed row_ptr: the row reads no entry
+        if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
+        e0 = e1 = 0;
     }
     for (int e = e0; e < e1; ++e) {
         const int jblk = a.col_idx[e];

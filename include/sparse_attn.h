@@ -230,7 +230,8 @@ int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_mask_params* 
  * counts it).  A row that keeps no key gets NaN and dev_status is set to
  * SA_ERR_EMPTY_ROW.  CSR entries at positions >= p->col_cap are ignored and
  * set SA_ERR_CAPACITY; a column outside [0, n_kb) is ignored and sets
- * SA_ERR_INVALID_ARGUMENT.
+ * SA_ERR_INVALID_ARGUMENT, and so does a negative row_ptr entry (its row then
+ * reads no entry).  With several conditions the last one written stays.
  * Optional (NULL = not written): pv_skip device uint8 [nnz * ceil(block_q/32)]
  * (G = ceil(block_q/32) flags per CSR entry, col_cap entries)
  * with pv_skip[e*G + g] = 1 when group g skipped the PV of CSR entry e;

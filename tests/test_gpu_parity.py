@@ -299,6 +299,51 @@ def test_empty_row_gives_nan_and_status():
     assert np.isfinite(o[0, 0, :128]).all()
 
 
+@pytest.mark.parametrize("name,lam", [("tiny", None), ("image_s", None), ("image_s_lam", -8.0),
+                                      ("long_video_s", None), ("long_video_s", -8.0)])
+def test_malformed_csr_is_contained(name, lam):
+    """A column outside [0, n_kb) and a negative row_ptr entry, on every attention kernel:
+    the bad column is skipped (its row equals the row without it), the two rows the
+    negative entry bounds come out NaN, the status word reports it, and every other row is
+    unchanged."""
+    w = rep(SMALL[name], lam=lam)
+    cfg = sa.config_from_workload(w)
+    rows, n_kb, n_qb = cfg.rows, cfg.n_kb, cfg.n_qb
+    log(f"[csr] {name}: lam={lam} bq={w.block_q} bk={w.block_k} rows={rows} n_kb={n_kb}")
+    assert rows >= 3
+    bad_col_row, neg = 0, rows - 1  # rp[rows - 1] < 0 bounds rows rows-2 and rows-1
+    q, k, v = generate(w)
+    outs = []
+    for bad in (False, True):
+        path = sa.SparseAttentionPath(cfg)
+        path.permute(dev(q), dev(k), dev(v))
+        cols, rp = [], np.zeros(rows + 1, dtype=np.int32)
+        for r in range(rows):
+            c = [0] if r % n_kb == 0 else [0, r % n_kb]
+            if r == bad_col_row:
+                c = [0, n_kb + 5] if bad else [0]
+            cols += c
+            rp[r + 1] = len(cols)
+        if bad:
+            rp[neg] = -1
+        path.row_ptr.copy_(torch.from_numpy(rp))
+        path.col_idx[:len(cols)].copy_(torch.from_numpy(np.array(cols, dtype=np.int32)))
+        path.attend()
+        torch.cuda.synchronize()
+        outs.append((path.statuses()[1], path.o_perm.cpu().numpy()))
+    (st_ok, o_ok), (st_bad, o_bad) = outs
+    assert st_ok == sa.SA_OK
+    assert st_bad in (sa.SA_ERR_INVALID_ARGUMENT, sa.SA_ERR_EMPTY_ROW)
+    for r in range(rows):
+        bh, i = divmod(r, n_qb)
+        b, h = divmod(bh, w.Hq)
+        t0, t1 = i * w.block_q, min((i + 1) * w.block_q, w.N)
+        if r in (neg - 1, neg):
+            assert np.isnan(o_bad[b, h, t0:t1]).all(), r
+        else:
+            assert np.array_equal(o_bad[b, h, t0:t1], o_ok[b, h, t0:t1]), r
+
+
 def test_capacity_overflow_sets_status():
     w = SMALL["image_s"]
     cfg = sa.config_from_workload(w)
