@@ -63,6 +63,29 @@ SMALL = {
                              theta=None, lam=None, seed=109),
 }
 
+# Degenerate and ragged sizes: a single token, one partial query block, a last block of
+# one row or one key, on every attention kernel (16-blocks, 128/64 and 128/128 with and
+# without PV skip, causal, d = 64)
+_im = CONFIGS["image"]
+_ca = CONFIGS["causal_long"]
+_ti = CONFIGS["tiny"]
+EDGE = {
+    "edge_n1_128x64_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 1), block_k=64, lam=-8.0, seed=201),
+    "edge_n1_128x128": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 1), seed=202),
+    "edge_n1_16x16": rep(_ti, latent=(1, 1, 1), seed=203),
+    "edge_n65_128x64_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 65), block_k=64, lam=-8.0, seed=204),
+    "edge_n129_128x128_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 129), lam=-8.0, seed=205),
+    "edge_n129_128x64": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 129), block_k=64, seed=206),
+    "edge_n17_16x16_lam": rep(_ti, latent=(1, 1, 17), lam=-8.0, seed=207),
+    "edge_causal_n1": rep(_ca, Hq=2, Hkv=1, latent=(1, 1, 1), window_tokens=64, sink_front=1, block_k=64,
+                          seed=208),
+    "edge_causal_n130_lam": rep(_ca, Hq=2, Hkv=1, latent=(1, 1, 130), window_tokens=64, block_k=64, lam=-8.0,
+                                seed=209),
+    "edge_causal_n129_128x128": rep(_ca, Hq=2, Hkv=1, latent=(1, 1, 129), window_tokens=64, seed=210),
+    "edge_d64_n65_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 65), D=64, block_k=64, lam=-8.0, seed=211),
+}
+SMALL.update(EDGE)
+
 
 def library_tile_pattern(w):
     """The library's tile-window pattern of the workload (host), or None."""
