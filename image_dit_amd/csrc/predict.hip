@@ -260,6 +260,7 @@ __device__ inline bool causal_forced(const TopCdfArgs& a, const RowGeom& g, int 
 // in 32 bits, sums are exact and the cumulative mass is monotone; the
 // truncation moves a prefix sum by less than n_kb * 2^-31.
 constexpr float kFix = 2147483648.0f;
+constexpr float kLog2eF = 1.4426950408889634f;
 constexpr double kFixD = 2147483648.0;
 
 // Selection key of a candidate: its probability bits + 1 (so 0 < key < 2^30,
@@ -379,7 +380,10 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             if (4 * q + t < nv && xs[t] != kForcedKey) {
-                const float ev = expf(__uint_as_float(xs[t]) - cmax);
+                // base-2 exponential of the scaled logit (its rounding moves p by a few
+                // 1e-6 relative, far inside the band where ties and the tau cut count as
+                // borderline); the compiler keeps results below 2^-126 as denormals
+                const float ev = exp2f((__uint_as_float(xs[t]) - cmax) * kLog2eF);
                 xs[t] = __float_as_uint(ev);
                 esum += ev;
             }
