@@ -18,12 +18,15 @@ Prints ONE JSON line.  ``value`` is executed TFLOP/s of the whole step
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload (rank 0, N=1 only).
 
-Extra modes (for counter collection under rocprofv3, not for the JSON line):
-  --mode attn   only the sparse attention launch, repeated
-  --mode copy   a plain device copy of known size (HBM counter calibration)
+Extra modes (not the benchmark line):
+  --mode attn      only the sparse attention launch, repeated (for rocprofv3 counters)
+  --mode copy      a plain device copy of known size (HBM counter calibration)
+  --mode ceilings  what the box reaches outside this library: a bf16 GEMM through torch
+                   (hipBLASLt) and torch's dense flash attention at the workload's shape
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -47,7 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
-    ap.add_argument("--mode", default="path", choices=["path", "attn", "copy"])
+    ap.add_argument("--mode", default="path", choices=["path", "attn", "copy", "ceilings"])
+    ap.add_argument("--no-lambda", action="store_true", help="turn the workload's PV skip off")
     ap.add_argument("--form", default="gather", choices=["gather", "materialize"],
                     help="reorder inside the kernels' loads (bf16 inputs) or as separate copies")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -148,6 +152,49 @@ def cpu_baseline(w, path, q, k, v, budget_s):
                        f"on the first {nblk} query blocks over the GPU's CSR ({t_attn:.2f} s)")}
 
 
+def _event_ms(torch, f, reps):
+    f()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        f()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def ceilings(torch, w):
+    """Reference points outside the library on the same box: a square bf16 GEMM and torch's
+    dense flash attention (flash backend only, so no fallback runs) at the workload's shape."""
+    out = {"mode": "ceilings", "workload": w.name}
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = _event_ms(torch, lambda: torch.matmul(a, b), 20)
+    out["gemm_bf16"] = {"m=n=k": n, "ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / ms / 1e9, 1)}
+    del a, b
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+
+        q = torch.randn(w.B, w.Hq, w.N, w.D, device="cuda", dtype=torch.bfloat16)
+        k = torch.randn(w.B, w.Hq, w.N, w.D, device="cuda", dtype=torch.bfloat16)
+        v = torch.randn(w.B, w.Hq, w.N, w.D, device="cuda", dtype=torch.bfloat16)
+
+        def run():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=w.causal)
+
+        ms = _event_ms(torch, run, 5)
+        dense = 4.0 * w.B * w.Hq * w.D * (w.N * (w.N + 1) / 2 if w.causal else float(w.N) ** 2)
+        out["sdpa_flash"] = {"shape": [w.B, w.Hq, w.N, w.D], "causal": w.causal, "ms": round(ms, 3),
+                             "tflops": round(dense / ms / 1e9, 1)}
+    except Exception as e:  # the flash backend is not available for this device or shape
+        out["sdpa_flash"] = {"error": str(e).splitlines()[0][:200] if str(e) else type(e).__name__}
+    out["peak_bf16_tflops"] = PEAK_BF16_TFLOPS
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -175,6 +222,11 @@ def main():
     w = CONFIGS[args.workload]
     if args.sparsity is not None:
         w = w.with_sparsity(args.sparsity)
+    if args.no_lambda:
+        w = dataclasses.replace(w, lam=None)
+    if args.mode == "ceilings":
+        print(json.dumps(ceilings(torch, w)))
+        return
     cfg = sa.config_from_workload(w)
     gather = args.form == "gather" and w.dtype == "bf16"
     path = sa.SparseAttentionPath(cfg, materialize=not gather)
