@@ -17,9 +17,11 @@ sampled blocks and a single block elsewhere.
 
 Every output, reference or candidate, comes from the library's own entry
 points (``sa_predict_mask_gather`` for the candidate masks,
-``sa_sparse_attn_fwd_gather`` for both outputs); only the error sums use torch
-reductions on the device.  The selection rules themselves are plain host
-logic (``select_tau_theta``, ``select_lambda``).
+``sa_sparse_attn_fwd_gather`` for both outputs; with keys on a grid of their
+own, which the gather forms do not take, the materialising calls on copies
+reordered once); only the error sums use torch reductions on the device.  The
+selection rules themselves are plain host logic (``select_tau_theta``,
+``select_lambda``).
 """
 
 from dataclasses import dataclass, replace
@@ -113,7 +115,11 @@ class Calibrator:
         self.torch = torch
         self.cfg = cfg
         self.q, self.k, self.v = q, k, v
-        self.path = SparseAttentionPath(cfg, device=q.device, materialize=False)
+        # the gather form takes one permutation for queries and keys
+        self.gather = cfg.N_k == cfg.N and cfg.latent_k is None and cfg.txt_len_k is None
+        self.path = SparseAttentionPath(cfg, device=q.device, materialize=not self.gather)
+        if not self.gather:
+            self.path.permute(q, k, v)
         self.sampled = (None if sample_blocks_per_head is None
                         else sample_query_blocks(cfg, sample_blocks_per_head, seed))
         # token rows of O the error is measured on
@@ -146,7 +152,13 @@ class Calibrator:
         o = torch.empty((cfg.B, cfg.Hq, cfg.N, cfg.D), dtype=torch.float32, device=self.q.device)
         status = torch.zeros(1, dtype=torch.int32, device=self.q.device)
         ap = replace(cfg, lam=None).attn_params(len(ci))
-        L.sa_sparse_attn_fwd_gather(self.q, self.k, self.v, self.path.perm, o, ap, row_ptr, col_idx, status)
+        p = self.path
+        if self.gather:
+            L.sa_sparse_attn_fwd_gather(self.q, self.k, self.v, p.perm, o, ap, row_ptr, col_idx, status)
+        else:
+            o_perm = torch.empty_like(o)
+            L.sa_sparse_attn_fwd(p.qp, p.kp, p.vp, o_perm, ap, row_ptr, col_idx, status)
+            L.sa_unpermute(o_perm, o, p.perm)
         torch.cuda.synchronize()
         if int(status.item()) != L.SA_OK:
             raise L.SparseAttnError(int(status.item()), "dense reference")
@@ -160,8 +172,13 @@ class Calibrator:
         p.cfg = cfg
         p.mp = cfg.mask_params()
         p.ap = cfg.attn_params(p.col_cap)
-        p.predict_gather(self.q, self.k)
-        p.attend_gather(self.q, self.k, self.v)
+        if self.gather:
+            p.predict_gather(self.q, self.k)
+            p.attend_gather(self.q, self.k, self.v)
+        else:
+            p.predict()
+            p.attend()
+            p.unpermute()
         torch.cuda.synchronize()
         st = p.statuses()
         if st != (L.SA_OK, L.SA_OK):
