@@ -128,7 +128,59 @@ def run_path(w, sparsity="default"):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_path_parity(name):
-    w = SMALL[name]
+    check_path_parity(name, SMALL[name])
+
+
+def random_workload(seed):
+    """A seeded random configuration: reorder and generator of one of the four bf16
+    workloads, its shape, head dim, block pair, GQA ratio (causal generator), sinks,
+    causal window, tau / theta / sparsity / lambda, all within the compiled limits."""
+    rng = np.random.default_rng(seed)
+    base = ["image", "video", "long_video", "causal_long"][seed % 4]
+    w = CONFIGS[base]
+    D = int(rng.choice([64, 128]))
+    bk = int(rng.choice([64, 128]))
+    lam = [None, -8.0, -4.0][int(rng.integers(3))]
+    tau = None if rng.random() < 0.3 else float(rng.uniform(0.5, 0.99))
+    spars = float(rng.uniform(0.3, 0.9)) if (tau is None or rng.random() < 0.5) else None
+    theta = None if rng.random() < 0.5 else float(rng.uniform(0.2, 0.8))
+    kw = dict(D=D, block_k=bk, lam=lam, tau=tau, sparsity=spars, theta=theta, seed=1000 + seed)
+    if base == "causal_long":
+        hkv = int(rng.integers(1, 3))
+        N = int(rng.integers(100, 1500))
+        kw.update(Hkv=hkv, Hq=hkv * int(rng.choice([1, 2, 4])), latent=(1, 1, N),
+                  window_tokens=int(rng.choice([0, 64, 300])), sink_front=int(rng.integers(0, 8)))
+    else:
+        t, h, ww = int(rng.integers(1, 6)), int(rng.integers(2, 13)), int(rng.integers(3, 18))
+        txt = int(rng.choice([0, 8, 20])) if base == "video" else 0
+        kw.update(Hq=2, Hkv=2, B=int(rng.integers(1, 3)), latent=(t, h, ww), txt_len=txt)
+        # keys on a grid of half the width, or (video) tile windows; first-frame sink rows
+        ww_k = ww
+        extra = rng.random()
+        if extra < 0.25:
+            ww_k = max(3, ww // 2)
+            kw.update(latent_k=(t, h, ww_k))
+        elif extra < 0.5 and base == "video":
+            kw.update(tile=(2, 4, 4), tile_radius=(1, 1, 1))
+        if base == "video":
+            kw.update(window=(2, 4, 4), sink_front=h * ww_k if w.first_frame_sink else 0, sink_back=txt)
+            if rng.random() < 0.25:
+                kw.update(sink_rows=h * ww)
+    return rep(w, **kw)
+
+
+RANDOM = {f"random_{s}": random_workload(s) for s in range(64)}
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_config_parity(name):
+    w = RANDOM[name]
+    log(f"[random] {name}: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} D={w.D} bk={w.block_k} "
+        f"tau={w.tau} theta={w.theta} s={w.sparsity} lam={w.lam} causal={w.causal} W={w.window_tokens}")
+    check_path_parity(name, w)
+
+
+def check_path_parity(name, w):
     log(f"[parity] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} N_k={w.N_k} D={w.D} bq={w.block_q} bk={w.block_k}")
     path, (q, k, v), gmask, gsimq, gsimk = run_path(w)
     cfg = path.cfg
