@@ -505,12 +505,12 @@ def assert_forms_identical(a, b):
             assert False, key
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", list(SMALL) + [n for n, w in RANDOM.items() if w.N_k == w.N])
 def test_gather_form_bit_identical(name):
     """Reading q, k, v through the permutation inside the kernels gives the
     materialised path's CSR, mask, block statistics, skip flags, counters and
     outputs bit for bit."""
-    w = SMALL[name]
+    w = SMALL[name] if name in SMALL else RANDOM[name]
     cfg = sa.config_from_workload(w)
     log(f"[gather] {name}: N={w.N} D={w.D} bq={w.block_q} bk={w.block_k} lam={w.lam} causal={w.causal}")
     if w.N_k != w.N:
