@@ -4,6 +4,7 @@ Usage: python -m image_dit_amd.build   (always recompiles every source)
 """
 
 import os
+import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -53,7 +54,32 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    _build_example(verbose)
     return LIB
+
+
+DEMO = os.path.join(BUILD, "path_demo")
+
+
+def _build_example(verbose: bool) -> None:
+    """The plain-C caller of the whole path (examples/path_demo.c), linked against the
+    library through $ORIGIN so the pair can move together."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        if verbose:
+            print("gcc not found: examples/path_demo.c not built")
+        return
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = [gcc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-isystem", os.path.join(rocm, "include"),
+           os.path.join(PKG, "examples", "path_demo.c"), "-L", PKG, "-lsparse_attn",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/..",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", DEMO]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on examples/path_demo.c:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {DEMO}")
 
 
 if __name__ == "__main__":
