@@ -16,6 +16,8 @@
 #include <cfloat>
 #include <type_traits>
 
+#include <climits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- TopCdf
-constexpr int kGroupRows = 16;  // query blocks per workgroup: the N side of the score MFMA
+constexpr int kGroupRows = 16;  // most query blocks per workgroup: the N side of the score MFMA
 
 // Row stride (floats) of the LDS score tile: room for every key block plus a
 // pad, an odd number of 16-byte quads, so the 16 rows written by one float4
@@ -531,16 +533,16 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
 // histogram[256] u32 | column forcing bits[ceil(n_kb/32)] u32.
 constexpr int kTopcdfWaves = 8;
 template <int D>
-__global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls) {
+__global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls, int gr) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int32_t wave_tot[kTopcdfWaves];
     float* scores = reinterpret_cast<float*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(scores + kGroupRows * ls);
     uint32_t* colf = hist + kTopcdfWaves * 256;
 
-    const int groups = (a.n_qb + kGroupRows - 1) / kGroupRows;
+    const int groups = (a.n_qb + gr - 1) / gr;
     const int bh = blockIdx.x / groups;  // b * Hq + hq
-    const int i0 = (blockIdx.x - bh * groups) * kGroupRows;
+    const int i0 = (blockIdx.x - bh * groups) * gr;
     const int hq = bh % a.Hq;
     const int b = bh / a.Hq;
     const int hk = hq / (a.Hq / a.Hkv);
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     const float* simk = a.simk + kvh * a.n_kb;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int i_last = min(i0 + kGroupRows, a.n_qb) - 1;
+    const int i_last = min(i0 + gr, a.n_qb) - 1;
     const int ncols = row_geom(a, i_last).nv;  // columns any row of the group can see
 
     // column forcing as bits: word j/32 of the mask, one ballot per 64 blocks
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     int tot = 0;
     for (int rr = 2 * wave; rr < 2 * wave + 2; ++rr) {
         const int i = i0 + rr;
-        if (i >= a.n_qb) break;
+        if (rr >= gr || i >= a.n_qb) break;
         tot += select_row(a, bh, i, reinterpret_cast<uint32_t*>(scores + rr * ls), colf, hS, lane);
     }
     if (lane == 0) wave_tot[wave] = tot;
@@ -623,7 +625,7 @@ constexpr int kMaxWordsPerLane = SA_MAX_KEY_BLOCKS / 256;
 
 __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, const int32_t* __restrict__ counts,
                                              const int32_t* __restrict__ group_tot, int n_groups,
-                                             int groups_per_head, int n_qb, int n_kb, int64_t rows,
+                                             int groups_per_head, int gr, int n_qb, int n_kb, int64_t rows,
                                              int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
                                              int64_t col_cap, int32_t* dev_status) {
     __shared__ long long red[4];
@@ -638,8 +640,8 @@ __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, c
     s = wave_sum_ll(s);
     if (lane == 0) red[wave] = s;
     const int bh = g / groups_per_head;
-    const int i0 = (g - bh * groups_per_head) * kGroupRows;
-    const int nr = min(kGroupRows, n_qb - i0);
+    const int i0 = (g - bh * groups_per_head) * gr;
+    const int nr = min(gr, n_qb - i0);
     const int64_t r0 = int64_t(bh) * n_qb + i0;
     __syncthreads();
     if (wave == 0) {
@@ -711,7 +713,31 @@ __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, c
 
 }  // namespace
 
-int64_t topcdf_groups(int64_t bh, int64_t n_qb) { return bh * ((n_qb + kGroupRows - 1) / kGroupRows); }
+// Query blocks per TopCdf workgroup.  The kernel runs as one round of long
+// workgroups, so its time is that of the CU given the most rows: with
+// kDeviceCUs compute units taking workgroups in turn, that is
+// ceil(groups / kDeviceCUs) * rows per group, minimised here over 8..16 rows
+// (fewer would leave most of the score product's 16 columns unused; ties: the
+// larger group, whose rows share one pass over the key-block means).
+constexpr int64_t kDeviceCUs = 256;
+int topcdf_group_rows(int64_t bh, int64_t n_qb) {
+    int best = kGroupRows;
+    int64_t best_cost = INT64_MAX;
+    for (int g = kGroupRows; g >= kGroupRows / 2; --g) {
+        const int64_t groups = bh * ((n_qb + g - 1) / g);
+        const int64_t cost = (groups + kDeviceCUs - 1) / kDeviceCUs * g;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = g;
+        }
+    }
+    return best;
+}
+
+int64_t topcdf_groups(int64_t bh, int64_t n_qb) {
+    const int g = topcdf_group_rows(bh, n_qb);
+    return bh * ((n_qb + g - 1) / g);
+}
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk, int32_t* dev_status,
@@ -743,11 +769,12 @@ hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream) {
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t nwg = topcdf_groups(int64_t(a.B) * a.Hq, a.n_qb);
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
+    const int gr = topcdf_group_rows(int64_t(a.B) * a.Hq, a.n_qb);
     const dim3 block{64 * kTopcdfWaves, 1, 1};
     if (a.D == 128)
-        hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), block, lds, stream, a, ls);
+        hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), block, lds, stream, a, ls, gr);
     else
-        hipLaunchKernelGGL(k_topcdf<64>, dim3(unsigned(nwg)), block, lds, stream, a, ls);
+        hipLaunchKernelGGL(k_topcdf<64>, dim3(unsigned(nwg)), block, lds, stream, a, ls, gr);
     return hipGetLastError();
 }
 
@@ -756,9 +783,10 @@ hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t*
                       int32_t* dev_status, hipStream_t stream) {
     const int64_t n_groups = topcdf_groups(bh, n_qb);
     if (n_groups > INT32_MAX || n_kb > SA_MAX_KEY_BLOCKS) return hipErrorInvalidValue;
-    const int gph = (n_qb + kGroupRows - 1) / kGroupRows;
+    const int gr = topcdf_group_rows(bh, n_qb);
+    const int gph = (n_qb + gr - 1) / gr;
     hipLaunchKernelGGL(k_csr, dim3(unsigned(n_groups)), dim3(256), 0, stream, mask, counts, group_tot,
-                       int(n_groups), gph, n_qb, n_kb, bh * n_qb, row_ptr, col_idx, col_cap, dev_status);
+                       int(n_groups), gph, gr, n_qb, n_kb, bh * n_qb, row_ptr, col_idx, col_cap, dev_status);
     return hipGetLastError();
 }
 

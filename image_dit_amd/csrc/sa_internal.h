@@ -40,7 +40,7 @@ struct TopCdfArgs {
     const float* simk;
     uint8_t* mask;
     int32_t* counts;
-    int32_t* group_tot;  // kept blocks per group of 16 query blocks
+    int32_t* group_tot;  // kept blocks per group of query blocks (topcdf_group_rows)
     const uint8_t* forced;  // [n_qb][n_kb] forced block pattern shared by all heads, or null
     int B, Hq, Hkv, D;
     int64_t N;
