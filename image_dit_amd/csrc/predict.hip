@@ -5,7 +5,7 @@
 //   k_block_stats  one streaming pass over Q and K: per block the mean token
 //                  and the mean pairwise cosine ||mean_t x_t/||x_t||||^2.
 //                  HBM-bound: every byte of Q and K is read exactly once.
-//   k_topcdf       per group of 16 query blocks of one head: compressed
+//   k_topcdf       per group of 8..16 query blocks of one head: compressed
 //                  scores against every key-block mean on the fp32 matrix
 //                  cores, then per query block (a wavefront takes two) the
 //                  guard/sink/window forcing, the softmax over the candidates,
@@ -528,7 +528,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
     return cnt;
 }
 
-// Eight wavefronts per group of 16 query blocks; wavefront w selects query
+// Eight wavefronts per group of gr <= 16 query blocks; wavefront w selects query
 // blocks 2w and 2w+1.  Dynamic LDS: scores[16][ls] f32 | per wavefront:
 // histogram[256] u32 | column forcing bits[ceil(n_kb/32)] u32.
 constexpr int kTopcdfWaves = 8;
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
 }
 
 // ---------------------------------------------------------------- CSR
-// One workgroup per group of 16 query blocks (the TopCdf grouping).  Its
+// One workgroup per group of gr query blocks (the TopCdf grouping).  Its
 // first row offset is the sum of the totals of all earlier groups; the
 // group's own rows are scanned by one wavefront; then each wavefront
 // compacts four mask rows into ascending column lists.

@@ -180,8 +180,9 @@ size_t sa_predict_workspace_bytes(const sa_mask_params* p);
  * [B,Hkv,n_kb,D]; off[2] query-block similarity fp32 [B,Hq,n_qb];
  * off[3] key-block similarity fp32 [B,Hkv,n_kb]; off[4] block mask uint8
  * [B,Hq,n_qb,n_kb]; off[5] kept blocks per row int32 [B*Hq*n_qb],
- * followed by the kept blocks of each group of 16 consecutive query blocks of
- * one head, int32 [B*Hq*ceil(n_qb/16)].
+ * followed by the kept blocks of each group of g consecutive query blocks of
+ * one head, int32 [B*Hq*ceil(n_qb/g)], g in 8..16 chosen from B*Hq and n_qb
+ * (sa_predict_workspace_bytes accounts for it).
  * Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
 int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
 
