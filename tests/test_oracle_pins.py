@@ -637,3 +637,32 @@ def test_hilbert_plan_is_permutation_on_ragged_grid():
     h, w = np.divmod(rem, 53)
     steps = np.abs(np.diff(t)) + np.abs(np.diff(h)) + np.abs(np.diff(w))
     assert steps.mean() < 1.5
+
+
+def test_attend_head_over_a_csr_equals_the_restricted_softmax():
+    """The per-head driver of the block attention over a global CSR (row_base offset,
+    query blocks picked or all) gives, row for row, the restricted softmax of the
+    token mask that the CSR's blocks define; blocks it is not asked for stay NaN."""
+    rng = np.random.default_rng(17)
+    N, d, bq, bk = 70, 8, 16, 16
+    q, k, v = rng.normal(size=(N, d)), rng.normal(size=(N, d)), rng.normal(size=(N, 3))
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    blocks = rng.random((nqb, nkb)) < 0.5
+    blocks[np.arange(nqb), np.arange(nqb) % nkb] = True  # every row keeps a block
+    # a CSR that starts with two rows of another head, so row_base matters
+    rp, ci = [0, 1, 2], [0, 1]
+    for i in range(nqb):
+        cols = np.nonzero(blocks[i])[0]
+        ci += cols.tolist()
+        rp.append(rp[-1] + len(cols))
+    rp, ci = np.array(rp), np.array(ci)
+    tok = np.repeat(np.repeat(blocks, bq, axis=0), bk, axis=1)[:N, :N]
+    want, _ = A.restricted_attention(q, k, v, tok)
+    y, recs = F.attend_head(q, k, v, rp, ci, 2, bq, bk)
+    assert set(recs) == set(range(nqb))
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+    y2, _ = F.attend_head(q, k, v, rp, ci, 2, bq, bk, qblocks=[1, 3])
+    rows = np.zeros(N, dtype=bool)
+    rows[1 * bq:2 * bq] = rows[3 * bq:4 * bq] = True
+    assert np.allclose(y2[rows], want[rows], rtol=1e-12, atol=1e-12)
+    assert np.isnan(y2[~rows]).all()
