@@ -109,6 +109,32 @@ def _ptr(t):
     return None if t is None else c_void_p(t.data_ptr())
 
 
+def _need(*specs):
+    """Refuse tensors the C ABI would misread.  Each spec is (tensor, name, dtype names,
+    optional): every element type is checked first, then that every tensor is
+    contiguous and in device memory."""
+    import torch
+    for t, name, dts, optional in specs:
+        if t is None:
+            if not optional:
+                raise ValueError(f"{name} is required")
+            continue
+        want = tuple(getattr(torch, d) for d in dts)
+        if t.dtype not in want:
+            raise TypeError(f"{name}: dtype {t.dtype} not accepted (expected {' or '.join(dts)})")
+    for t, name, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _a(t, name, *dts, optional=False):
+    return (t, name, dts, optional)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -158,6 +184,9 @@ def sa_plan_tile_window(layout: SaLayout, tile, radius, block_q: int, block_k: i
 def sa_permute(x, y, perm, stream=None):
     """y[b,h,i,:] = bf16(x[b,h,perm[i],:]); x bf16 or fp32 [B,H,N,D]; y bf16 [B,H,N,D]."""
     import torch
+    _need(_a(x, "x", "float32", "bfloat16"), _a(y, "y", "bfloat16"), _a(perm, "perm", "int32"))
+    if tuple(y.shape) != tuple(x.shape) or perm.numel() != x.shape[2]:
+        raise ValueError("sa_permute: y must have x's shape and perm N entries")
     B, H, N, D = x.shape
     dt = SA_F32 if x.dtype == torch.float32 else SA_BF16
     code = lib().sa_permute(_ptr(x), dt, _ptr(y), _ptr(perm), B, H, N, D, _stream(stream))
@@ -166,6 +195,9 @@ def sa_permute(x, y, perm, stream=None):
 
 def sa_unpermute(y, x, perm, stream=None):
     """x[b,h,perm[i],:] = y[b,h,i,:]; fp32 [B,H,N,Dv]."""
+    _need(_a(y, "y", "float32"), _a(x, "x", "float32"), _a(perm, "perm", "int32"))
+    if tuple(y.shape) != tuple(x.shape) or perm.numel() != y.shape[2]:
+        raise ValueError("sa_unpermute: x must have y's shape and perm N entries")
     B, H, N, Dv = y.shape
     code = lib().sa_unpermute(_ptr(y), _ptr(x), _ptr(perm), B, H, N, Dv, _stream(stream))
     _check(code, "sa_unpermute")
@@ -197,6 +229,10 @@ def sa_predict_workspace_offsets(p: SaMaskParams):
 
 def sa_predict_mask(q, k, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mask_out=None, sim_q=None,
                     sim_k=None, stream=None):
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(ws, "ws", "uint8"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(mask_out, "mask_out", "uint8", optional=True), _a(sim_q, "sim_q", "float32", optional=True),
+          _a(sim_k, "sim_k", "float32", optional=True))
     code = lib().sa_predict_mask(_ptr(q), _ptr(k), ctypes.byref(p), _ptr(ws), ws.numel() * ws.element_size(),
                                  _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(mask_out), _ptr(sim_q),
                                  _ptr(sim_k), _ptr(dev_status), _stream(stream))
@@ -205,6 +241,9 @@ def sa_predict_mask(q, k, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mas
 
 def sa_sparse_attn_fwd(q, k, v, o, p: SaAttnParams, row_ptr, col_idx, dev_status, pv_skip=None,
                        counters=None, stream=None):
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(v, "v", "bfloat16"), _a(o, "o", "float32"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(pv_skip, "pv_skip", "uint8", optional=True), _a(counters, "counters", "int64", optional=True))
     code = lib().sa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), ctypes.byref(p), _ptr(row_ptr),
                                     _ptr(col_idx), _ptr(pv_skip), _ptr(counters), _ptr(dev_status),
                                     _stream(stream))
@@ -214,6 +253,10 @@ def sa_sparse_attn_fwd(q, k, v, o, p: SaAttnParams, row_ptr, col_idx, dev_status
 def sa_predict_mask_gather(q, k, perm, p: SaMaskParams, ws, row_ptr, col_idx, dev_status, mask_out=None,
                            sim_q=None, sim_k=None, stream=None):
     """sa_predict_mask on q[:, :, perm], k[:, :, perm] without materialising them (q, k bf16, original order)."""
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(perm, "perm", "int32"), _a(ws, "ws", "uint8"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(mask_out, "mask_out", "uint8", optional=True), _a(sim_q, "sim_q", "float32", optional=True),
+          _a(sim_k, "sim_k", "float32", optional=True))
     code = lib().sa_predict_mask_gather(_ptr(q), _ptr(k), _ptr(perm), ctypes.byref(p), _ptr(ws),
                                         ws.numel() * ws.element_size(), _ptr(row_ptr), _ptr(col_idx),
                                         col_idx.numel(), _ptr(mask_out), _ptr(sim_q), _ptr(sim_k),
@@ -225,6 +268,10 @@ def sa_predict_mask_ex(q, k, perm, forced, p: SaMaskParams, ws, row_ptr, col_idx
                        sim_q=None, sim_k=None, stream=None):
     """sa_predict_mask with an optional permutation (None: q, k already reordered) and an
     optional forced block pattern (device uint8 [n_qb, n_kb], shared by all heads)."""
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(perm, "perm", "int32", optional=True), _a(ws, "ws", "uint8"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(mask_out, "mask_out", "uint8", optional=True), _a(sim_q, "sim_q", "float32", optional=True),
+          _a(sim_k, "sim_k", "float32", optional=True), _a(forced, "forced", "uint8", optional=True))
     code = lib().sa_predict_mask_ex(_ptr(q), _ptr(k), _ptr(perm), _ptr(forced), ctypes.byref(p), _ptr(ws),
                                     ws.numel() * ws.element_size(), _ptr(row_ptr), _ptr(col_idx),
                                     col_idx.numel(), _ptr(mask_out), _ptr(sim_q), _ptr(sim_k),
@@ -235,6 +282,9 @@ def sa_predict_mask_ex(q, k, perm, forced, p: SaMaskParams, ws, row_ptr, col_idx
 def sa_sparse_attn_fwd_gather(q, k, v, perm, o, p: SaAttnParams, row_ptr, col_idx, dev_status, pv_skip=None,
                               counters=None, stream=None):
     """sa_sparse_attn_fwd on the reordered q, k, v, with o written back in the original order."""
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(v, "v", "bfloat16"), _a(perm, "perm", "int32"), _a(o, "o", "float32"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(pv_skip, "pv_skip", "uint8", optional=True), _a(counters, "counters", "int64", optional=True))
     code = lib().sa_sparse_attn_fwd_gather(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(o), ctypes.byref(p),
                                            _ptr(row_ptr), _ptr(col_idx), _ptr(pv_skip), _ptr(counters),
                                            _ptr(dev_status), _stream(stream))

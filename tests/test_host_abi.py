@@ -348,3 +348,32 @@ def test_permute_rejects_invalid_arguments():
     # one int32 (row, chunk) index per thread
     assert L.sa_permute(FAKE, sa.SA_BF16, FAKE, FAKE, 1, 1, 1 << 26, 256, None) == sa.SA_ERR_UNSUPPORTED
     assert L.sa_unpermute(FAKE, FAKE, FAKE, 1, 1, 1 << 26, 128, None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_tensors_the_abi_would_misread():
+    """The Python binding checks element type, contiguity and device before any call:
+    an fp16 tensor is not silently read as bf16, an int64 permutation is not read as
+    int32, a strided view is refused, and host memory is refused (no GPU needed)."""
+    import torch
+
+    x = torch.zeros((1, 2, 8, 16), dtype=torch.float16)
+    y = torch.zeros((1, 2, 8, 16), dtype=torch.bfloat16)
+    perm = torch.arange(8, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        sa.sa_permute(x, y, perm)
+    with pytest.raises(TypeError):
+        sa.sa_permute(x.float(), y, perm.long())
+    with pytest.raises(ValueError, match="contiguous"):
+        sa.sa_permute(torch.zeros((1, 2, 16, 8), dtype=torch.float32).transpose(2, 3), y, perm)
+    with pytest.raises(ValueError, match="device"):
+        sa.sa_permute(x.float(), y, perm)
+    o = torch.zeros((1, 2, 8, 16), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        sa.sa_unpermute(o.double(), o, perm)
+    p = sa.make_attn_params(1, 2, 2, 8, 16, 128, 64)
+    rp = torch.zeros(3, dtype=torch.int32)
+    st = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        sa.sa_sparse_attn_fwd(y.half(), y, y, o, p, rp, rp, st)
+    with pytest.raises(TypeError):
+        sa.sa_sparse_attn_fwd(y, y, y, o, p, rp.long(), rp, st)
