@@ -2,8 +2,9 @@
 
 The whole path runs exactly as the benchmark runs it.  The oracle then checks
 what it can afford one by one: the full permutation and sampled permuted
-rows (bit-exact), the block statistics and predicted mask rows of sampled
-heads (exact except borderline rows), the full CSR against the GPU's own
+rows (bit-exact), the block statistics and the predicted mask rows of the
+first head in full and of the last head on a sample (each row the oracle's, or
+one it allows at a flagged near-boundary decision), the full CSR against the GPU's own
 mask (bit-exact), the counters against the CSR and skip flags, and the
 outputs of sampled query blocks against fp64 on the GPU's CSR.
 """
@@ -97,22 +98,28 @@ def test_full_size_sampled_parity(name):
     mp = R.mask_params(w)
     G = w.Hq // w.Hkv
     o = path.o.cpu().numpy() if w.B * w.Hq * w.N * w.D < 2e8 else None
+    # the first head row by row in full, the last head on 24 sampled query blocks
     heads = [(0, 0), (w.B - 1, w.Hq - 1)]
     n_bad = n_border = n_rows = 0
+    flagged = {"tau": 0, "theta": 0, "tie": 0}
     worst_max, sum_abs, n_el = 0.0, 0.0, 0
-    for b, h in heads:
+    for hi, (b, h) in enumerate(heads):
         hk = h // G
         qp = R.permuted(q[b, h], perm)
         kp = R.permuted(k[b, hk], perm_k)
         vp = R.permuted(v[b, hk], perm_k)
-        rows = sorted(set(np.linspace(0, cfg.n_qb - 1, 24).astype(int).tolist()))
+        rows = list(range(cfg.n_qb)) if hi == 0 else \
+            sorted(set(np.linspace(0, cfg.n_qb - 1, 24).astype(int).tolist()))
         ref = OP.predict_head(qp, kp, mp, rows=rows)
         r0 = (b * w.Hq + h) * cfg.n_qb
         gm = gmask[r0:r0 + cfg.n_qb]
-        bad, border, checked = R.compare_head_mask(gm, ref, rows)
+        bad, border, checked, _ = R.compare_head_mask(gm, ref, mp, rows)
+        for kk, c in R.borderline_counts(ref, rows).items():
+            flagged[kk] += c
         n_bad += len(bad)
         n_border += len(border)
         n_rows += checked
+        rows = sorted(set(np.linspace(0, cfg.n_qb - 1, 24).astype(int).tolist()))
         qbar = path.workspace_view(0, torch.float32, (cfg.B, cfg.Hq, cfg.n_qb, cfg.D))[b, h].cpu().numpy()
         assert np.allclose(qbar, ref["qbar"], rtol=1e-5, atol=1e-5)
         qblocks = rows[:: max(1, len(rows) // 6)]
@@ -130,7 +137,8 @@ def test_full_size_sampled_parity(name):
                 assert far == 0
     if name.startswith("max_blocks"):
         assert cfg.n_kb == sa.SA_MAX_KEY_BLOCKS
-    log(f"[full] {name}: nnz={int(rp[-1])} sampled_rows={n_rows} mismatch={n_bad} borderline={n_border} "
+    log(f"[full] {name}: nnz={int(rp[-1])} checked_rows={n_rows} mismatch={n_bad} differing_borderline={n_border} "
+        f"flagged={flagged} "
         f"out_max={worst_max:.3e} out_mean={sum_abs / n_el:.3e} pv_exec={cnt[1]} pv_skip={cnt[2]}")
     assert n_bad == 0
     assert worst_max <= R.MAX_ABS and sum_abs / n_el <= R.MEAN_ABS

@@ -233,16 +233,12 @@ def check_path_parity(name, w):
                     assert np.array_equal(gmask[r0 + i], OP._valid_blocks(i, mp)), i
                 if mp.forced is not None:
                     assert np.all(gmask[r0 + i][mp.forced[i] & OP._valid_blocks(i, mp)]), i
-            bad, border, checked = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref)
+            # every row equals the oracle row, or one the oracle allows by taking a flagged
+            # near-boundary decision the other way (forced blocks always agree)
+            bad, border, checked, _ = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref, mp)
             n_bad += len(bad)
             n_border += len(border)
             n_rows += checked
-            for i in border:  # a borderline row keeps its forced blocks and differs by at most a swap
-                if "theta" in ref["info"][i]["border"]:
-                    continue
-                forced = OP._forced_blocks(i, mp, ref["simk"], OP._valid_blocks(i, mp))
-                assert np.all(gmask[r0 + i][forced])
-                assert np.count_nonzero(gmask[r0 + i] != ref["mask"][i]) <= 2
             # (a5) attention on the GPU's CSR, PV decisions replayed
             ys, recs = R.attend_rows(qp[b, h], kp[b, hk], vp[b, hk], w, rp, ci, r0, range(cfg.n_qb),
                                      skip, groups)

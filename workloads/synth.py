@@ -146,15 +146,43 @@ def _gen_iid_bf16(cfg: Workload):
     return bf16_bits(q), bf16_bits(k), bf16_bits(v)
 
 
+def _gen_frame_position(cfg: Workload):
+    """The teaching video of the SparseAttn article (section 04) widened to head dim D:
+    4 frames of 4x4 positions in frame-major order; query head h carries amplitude 6 on
+    the one-hot of the token's frame (h even, dims 0..t-1) or of its position (h odd,
+    dims t..t+h*w-1); every dim gets N(0, 0.15^2) noise; K equals Q; V ~ N(0, 1).
+    float32, like the tiny workload."""
+    t, hh, ww = cfg.latent
+    P = hh * ww
+    N = t * P
+    if cfg.txt_len or cfg.N != N or cfg.D < t + P or cfg.Hq != cfg.Hkv:
+        raise ValueError("the frame/position construction needs a bare video grid, D >= t + h*w, Hq == Hkv")
+    rng = np.random.default_rng(cfg.seed)
+    frame = np.arange(N) // P
+    pos = np.arange(N) % P
+    q = np.zeros((cfg.B, cfg.Hq, N, cfg.D), dtype=np.float64)
+    for h in range(cfg.Hq):
+        if h % 2 == 0:
+            q[:, h, np.arange(N), frame] = 6.0
+        else:
+            q[:, h, np.arange(N), t + pos] = 6.0
+    q = (q + rng.normal(0.0, 0.15, size=q.shape)).astype(np.float32)
+    v = rng.standard_normal((cfg.B, cfg.Hkv, N, cfg.D)).astype(np.float32)
+    return q, q.copy(), v
+
+
 def generate(cfg: Workload, kind: str = "auto"):
     """Return (q, k, v) numpy arrays in BNSD, in the ORIGINAL token order.
 
     bf16 workloads return uint16 bit patterns; the tiny workload returns float32.
     ``kind`` overrides the recipe: "iid" draws iid N(0,1) (bf16 unless the
-    workload is fp32), used for shape sweeps in tests.
+    workload is fp32), used for shape sweeps in tests; "frame_position" is the
+    structured teaching input (fp32, see _gen_frame_position).
     """
     if kind == "iid":
         return _gen_iid_f32(cfg) if cfg.dtype == "f32" else _gen_iid_bf16(cfg)
+    if kind == "frame_position":
+        return _gen_frame_position(cfg)
     if cfg.name == "tiny" or cfg.dtype == "f32":
         return _gen_iid_f32(cfg)
     if cfg.name == "causal_long":
