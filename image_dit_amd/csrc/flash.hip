@@ -399,6 +399,7 @@ __device__ inline void dma_wait() {
 }
 
 constexpr int kRing = 8;  // LDS ring of per-tile source rows (GATHER)
+constexpr int kColChunk = 512;  // column indices staged in LDS per chunk (k_flash_lam)
 
 // Per-lane part of the tile DMA.  Instruction c of wave w moves rows
 // 8*rg .. 8*rg+7 (rg = 2w + c/SEG) of 128-byte segment c % SEG of a 64-row
@@ -752,6 +753,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     __shared__ __align__(16) uint16_t Vs[BK * D];
     __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
     __shared__ uint32_t need[3];  // need[t % 3] bit w: wave w keeps the PV product of tile t
+    // the row's column indices, kColChunk tiles per chunk, two chunks in turn
+    __shared__ __align__(16) int32_t colc[2][kColChunk];
 
     const int G = a.B * a.Hq * a.n_qb;
     const int per = (G + 7) >> 3;
@@ -811,11 +814,13 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const uint32_t pr_lds = lds_addr(&prow[0][0]);
     const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DI * 1024);
     const uint32_t vs_lds = lds_addr(&Vs[0]) + uint32_t(wave * DI * 1024);
-    // wave 0 fetches the source rows of tile t (first key key0) into ring slot t % kRing
+    // wave 0 fetches the source rows of tile t (first key key0) into ring slot t % kRing;
+    // a tile past the row's end (key -1) reads zeros
     auto issue_perm = [&](int t, int key0) {
         if constexpr (GATHER) {
-            if (wave == 0 && key0 >= 0)
-                dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4), uint32_t(key0 + lane) * 4u);
+            if (wave == 0)
+                dma4_at(rP, pr_lds + uint32_t((t % kRing) * BK * 4),
+                        key0 >= 0 ? uint32_t(key0 + lane) * 4u : 0x80000000u);
         }
     };
     // A tile's rows for this lane: its first key and the ring entries of the
@@ -906,15 +911,28 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
         }
     };
-    auto any_need = [&](int slot) { return __builtin_amdgcn_readfirstlane(need[slot]) != 0u; };
 
+    // column indices of tiles 0 .. 2*kColChunk-1 (published by the barrier before the
+    // loop); later chunks are DMA'd by wave 0 one chunk ahead.  No scalar loads stay in
+    // the loop: an outstanding one would make every LDS-operand wait a full lgkmcnt(0).
+    {
+        constexpr int PER = 2 * kColChunk / 256;
+        int cv[PER];
+#pragma unroll
+        for (int x = 0; x < PER; ++x) cv[x] = tid + 256 * x < nt ? col_idx[e0 + tid + 256 * x] : -1;
+#pragma unroll
+        for (int x = 0; x < PER; ++x) (&colc[0][0])[tid + 256 * x] = cv[x];
+    }
+    const int4v rC = head_desc(col_idx + (nt > 0 ? e0 : 0), uint32_t(nt) * 4u);
     // kr: source rows of the next K tile to fetch (t+2 during iteration t);
     // vr: those of tile t-1, whose V may be fetched during iteration t
     Rows kr, vr;
-    // first keys of tiles t .. t+3 (one column index is loaded per iteration,
-    // ahead of the ring reads, so waiting for it never waits for them)
+    // first keys of tiles t .. t+4: the column index of tile t+5 is loaded
+    // during iteration t and first used in iteration t+1, so its scalar load
+    // has a whole iteration to land
     int kc = nt > 0 ? tile_key0(0) : -1, k1 = nt > 1 ? tile_key0(1) : -1;
     int k2 = nt > 2 ? tile_key0(2) : -1, k3 = nt > 3 ? tile_key0(3) : -1;
+    int k4 = nt > 4 ? tile_key0(4) : -1;
     if constexpr (GATHER) {
         issue_perm(0, kc);
         issue_perm(1, k1);
@@ -937,32 +955,44 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     __syncthreads();
     q_ready(qf);
     int kbuf = 0;  // t % 3, also the need slot of tile t
+    uint32_t need_prev = 0u;  // the need flags of tile t-1, read after the last barrier
+    uint64_t skipm = 0ull;    // bit i: PV of tile t - t % 64 + i skipped (this wave's group)
     for (int t = 0; t < nt; ++t) {
         const int kb0 = kc;
-        const int k4 = t + 4 < nt ? tile_key0(t + 4) : -1;
-        const int slot_prev = kbuf == 0 ? 2 : kbuf - 1;  // (t - 1) % 3
         const int slot_next = kbuf == 2 ? 0 : kbuf + 1;  // (t + 1) % 3 == (t - 2) % 3
         // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
-        const bool vprev = t > 0 && any_need(slot_prev);
+        const uint32_t need_s = __builtin_amdgcn_readfirstlane(need_prev);
+        const bool vprev = t > 0 && need_s != 0u;
+        // raw column index of tile t+5 (LDS), checked and turned into a key at the end
+        // of the iteration
+        int c5v = colc[((t + 5) / kColChunk) & 1][(t + 5) % kColChunk];  // stale past the row's end
+        // the chunk after next: tiles t+kColChunk.., into the buffer of the chunk that
+        // ended with tile t-1 (its last read was in iteration t-6); issued before the
+        // V and K tiles so the waits below cover it
+        if (wave == 0 && t > 0 && (t % kColChunk) == 0 && t + kColChunk < nt) {
+            const uint32_t cl = lds_addr(&colc[((t / kColChunk) + 1) & 1][0]);
+#pragma unroll
+            for (int h = 0; h < kColChunk / 256; ++h)
+                dma16_at(rC, cl + uint32_t(h * 1024), uint32_t(t + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
+        }
         // the mask of tile t-2 was read during iteration t-1: clear it for tile t+1
         if (tid == 0) need[slot_next] = 0u;
-        if (GATHER && t + 4 < nt) issue_perm(t + 4, k4);
+        // prefetches past the row's end (key -1) read zeros into buffers nobody reads,
+        // so they need no condition
+        if (GATHER) issue_perm(t + 4, k4);
         if (vprev) issue_v(vr);
-        const bool kpre = t + 2 < nt;
-        if (kpre) issue_k(kr, kbuf == 0 ? 2 : kbuf - 1);
+        issue_k(kr, kbuf == 0 ? 2 : kbuf - 1);
         // rows for the next iteration: V of tile t, K of tile t+3 (its ring
         // slot was filled during iteration t-1)
         tile_rows(kb0, t, vr);
-        if (t + 3 < nt) tile_rows(k3, t + 3, kr);
+        tile_rows(k3, t + 3, kr);
 
         int my_need = 0;
         float alpha = 1.f;
         floatx16 s0, s1;
         if (kb0 < 0) {
             bad_col = true;
-        } else if (!wave_rows) {
-            if (pv_skip && lane == 0) pv_skip[int64_t(e0 + t) * 4 + wave] = 0;
-        } else {
+        } else if (wave_rows) {
             const uint16_t* K = Ks[kbuf];
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
@@ -1013,8 +1043,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
             for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
             l_part = fmaf(l_part, alpha, ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
-            if (pv_skip && lane == 0) pv_skip[int64_t(e0 + t) * 4 + wave] = skip ? 1 : 0;
             if (skip) {
+                skipm |= 1ull << (t & 63);
                 ++n_skip;
             } else {
                 ++n_exec;
@@ -1023,8 +1053,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         }
         // PV of tile t-1 once every wave's part of its V tile has landed
         if (vprev) {
-            if (kpre) dma_wait<DI>();
-            else dma_wait<0>();
+            dma_wait<DI>();
             tile_barrier();
             if (pend) apply_pending();
         }
@@ -1041,19 +1070,32 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             palpha = alpha;
         }
         if (lane == 0 && my_need) atomicOr(&need[kbuf], 1u << wave);
+        // the skip flags of 64 tiles leave in one store (lane i: tile t - t % 64 + i)
+        if (pv_skip && ((t & 63) == 63 || t == nt - 1)) {
+            if (lane <= (t & 63)) pv_skip[int64_t(e0 + (t & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
+            skipm = 0ull;
+        }
         // K of tile t+1 and the source rows of tile t+4 have landed (K of t+2
         // may be in flight); V reads and the need flags are complete
-        if (kpre) dma_wait<DI>();
-        else dma_wait<0>();
+        dma_wait<DI>();
         lds_wait();
         tile_barrier();
+        // every wave's need flag of tile t is in place: read it now, use it at the
+        // top of the next iteration
+        need_prev = need[kbuf];
         kbuf = kbuf == 2 ? 0 : kbuf + 1;
         kc = k1;
         k1 = k2;
         k2 = k3;
         k3 = k4;
+        // the LDS read of c5v is consumed only here (the empty asm keeps the
+        // compiler from moving the read-first-lane, and its wait, up to the read)
+        asm volatile("" : "+v"(c5v));
+        const int c5 = __builtin_amdgcn_readfirstlane(c5v);
+        k4 = (t + 5 >= nt || c5 < 0 || c5 >= a.n_kb) ? -1 : c5 * BK;
     }
-    if (nt > 0 && any_need(kbuf == 0 ? 2 : kbuf - 1)) {
+    dma_wait<0>();  // no LDS write may land after the workgroup ends
+    if (nt > 0 && __builtin_amdgcn_readfirstlane(need_prev) != 0u) {
         issue_v(vr);
         dma_wait<0>();
         tile_barrier();
