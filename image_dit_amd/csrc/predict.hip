@@ -27,26 +27,31 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+// Wave-wide reductions without LDS traffic: DPP within each row of 16 lanes
+// (quad swaps, then the other quad of 8, then the other 8 of 16), then the
+// four row totals through read-lane.  The result is wave-uniform.
+template <int CTRL>
+__device__ inline uint32_t dpp_all(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xf, 0xf, false));
 }
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+template <class T, class F>
+__device__ inline T wave_reduce(T v, F op) {
+    auto mv = [](T x, auto ctrl) {
+        return __builtin_bit_cast(T, dpp_all<decltype(ctrl)::value>(__builtin_bit_cast(uint32_t, x)));
+    };
+    v = op(v, mv(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+    v = op(v, mv(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+    v = op(v, mv(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    v = op(v, mv(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+    auto rl = [](T x, int l) {
+        return __builtin_bit_cast(T, uint32_t(__builtin_amdgcn_readlane(int(__builtin_bit_cast(uint32_t, x)), l)));
+    };
+    return op(op(rl(v, 0), rl(v, 16)), op(rl(v, 32), rl(v, 48)));
 }
-__device__ inline int wave_sum_i(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
-__device__ inline uint32_t wave_sum_u(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
+__device__ inline float wave_sum(float v) { return wave_reduce(v, [](float x, float y) { return x + y; }); }
+__device__ inline float wave_max(float v) { return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); }); }
+__device__ inline int wave_sum_i(int v) { return wave_reduce(v, [](int x, int y) { return x + y; }); }
+__device__ inline uint32_t wave_sum_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; }); }
 __device__ inline long long wave_sum_ll(long long v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
@@ -338,12 +343,12 @@ __device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pr
 // over the radix digits of the keys (the TopCdf search carries the mass per
 // bin, the floor search the count), so no sort is needed.  Returns the row's
 // kept count.
-__device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, const uint32_t* colf,
+__device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint32_t* row, const uint32_t* colf,
                           uint32_t* hS, int lane) {
     const RowGeom g = row_geom(a, i);
     const int64_t grow = int64_t(bh) * a.n_qb + i;
     // low-similarity query blocks and sink rows keep their whole valid row
-    const bool forced_row = (a.theta > 0.f && a.simq[grow] < a.theta) || g.q_first < a.sink_rows;
+    const bool forced_row = (a.theta > 0.f && simq_i < a.theta) || g.q_first < a.sink_rows;
     const int nv = g.nv;
     uint4* row4 = reinterpret_cast<uint4*>(row);
 
@@ -495,6 +500,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
         quota = x_rem;
     }
     uint8_t* out = a.mask + grow * a.n_kb;
+    const bool aligned4 = (a.n_kb & 3) == 0;
     const unsigned long long below = (1ull << lane) - 1ull;
     uint32_t run = 0;
     for (int q0 = 0; 4 * q0 < a.n_kb; q0 += 64) {
@@ -513,14 +519,24 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, uint32_t* row, con
             before += uint32_t(__popcll(em[t] & below));
         }
         uint32_t rank = before;
+        uint32_t word = 0;  // the mask bytes of blocks 4q .. 4q+3
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int j = 4 * q + t;
             const uint32_t kk = j < nv ? xs[t] : 0u;
             const bool kept = cand[t] && (kk > v_thr || (eq[t] && rank < quota));
             if (eq[t]) ++rank;
-            if (j < a.n_kb) out[j] = forced_row ? uint8_t(j < nv) : uint8_t(kk == kForcedKey || kept);
+            const uint32_t bit = forced_row ? uint32_t(j < nv) : uint32_t(kk == kForcedKey || kept);
+            word |= bit << (8 * t);
             run += uint32_t(__popcll(em[t]));
+        }
+        // one 4-byte store per lane when the row starts 4-byte aligned (n_kb % 4 == 0)
+        if (aligned4) {
+            if (4 * q < a.n_kb) reinterpret_cast<uint32_t*>(out)[q] = word;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (4 * q + t < a.n_kb) out[4 * q + t] = uint8_t(word >> (8 * t));
         }
     }
     const int cnt = forced_row ? nv : n_forced + keep;
@@ -536,6 +552,7 @@ template <int D>
 __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls, int gr) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int32_t wave_tot[kTopcdfWaves];
+    __shared__ float simq_g[kGroupRows];
     float* scores = reinterpret_cast<float*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(scores + kGroupRows * ls);
     uint32_t* colf = hist + kTopcdfWaves * 256;
@@ -554,6 +571,9 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     const int i_last = min(i0 + gr, a.n_qb) - 1;
     const int ncols = row_geom(a, i_last).nv;  // columns any row of the group can see
 
+    // the group's query-block similarities, loaded once while the scores are computed
+    if (threadIdx.x < kGroupRows)
+        simq_g[threadIdx.x] = a.simq[int64_t(bh) * a.n_qb + min(i0 + int(threadIdx.x), a.n_qb - 1)];
     // column forcing as bits: word j/32 of the mask, one ballot per 64 blocks
     for (int j0 = 64 * wave; j0 < ncols; j0 += 64 * kTopcdfWaves) {
         const int j = j0 + lane;
@@ -604,7 +624,7 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     for (int rr = 2 * wave; rr < 2 * wave + 2; ++rr) {
         const int i = i0 + rr;
         if (rr >= gr || i >= a.n_qb) break;
-        tot += select_row(a, bh, i, reinterpret_cast<uint32_t*>(scores + rr * ls), colf, hS, lane);
+        tot += select_row(a, bh, i, simq_g[rr], reinterpret_cast<uint32_t*>(scores + rr * ls), colf, hS, lane);
     }
     if (lane == 0) wave_tot[wave] = tot;
     __syncthreads();
