@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     SA_ERR_UNSUPPORTED, SA_F32, SA_MAX_KEY_BLOCKS, SA_OK, SA_ORDER_HILBERT, SA_ORDER_IDENTITY,
     SA_ORDER_WINDOW, SA_PV_GROUP_ROWS, SaAttnParams, SaLayout, SaMaskParams, SparseAttnError, lib,
     make_attn_params, make_layout, make_mask_params, sa_permute, sa_plan_permutation, sa_plan_tile_window,
-    sa_predict_mask, sa_predict_mask_ex,
+    sa_predict_mask, sa_predict_mask_ex, sa_predict_mask_gather_noalloc, SA_NOALLOC_SCRATCH_BYTES,
     sa_predict_workspace_bytes, sa_predict_workspace_offsets, sa_sparse_attn_fwd, sa_status_string,
     sa_unpermute)
 from .pipeline import PathConfig, SparseAttentionPath, config_from_workload  # noqa: F401

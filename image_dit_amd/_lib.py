@@ -25,11 +25,12 @@ SA_ORDER_WINDOW = 1
 SA_ORDER_HILBERT = 2
 SA_PV_GROUP_ROWS = 32
 SA_MAX_KEY_BLOCKS = 2048
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermute",
            "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
            "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather",
-           "sa_plan_tile_window", "sa_predict_mask_ex")
+           "sa_plan_tile_window", "sa_predict_mask_ex", "sa_predict_mask_gather_noalloc")
 
 
 class SaLayout(ctypes.Structure):
@@ -101,6 +102,10 @@ def lib() -> ctypes.CDLL:
                                      c_size_t, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p]
     L.sa_predict_mask_ex.restype = c_int
+    L.sa_predict_mask_gather_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(SaMaskParams), c_void_p,
+                                                 c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                 c_void_p]
+    L.sa_predict_mask_gather_noalloc.restype = c_int
     _lib = L
     return L
 
@@ -289,3 +294,16 @@ def sa_sparse_attn_fwd_gather(q, k, v, perm, o, p: SaAttnParams, row_ptr, col_id
                                            _ptr(row_ptr), _ptr(col_idx), _ptr(pv_skip), _ptr(counters),
                                            _ptr(dev_status), _stream(stream))
     _check(code, "sa_sparse_attn_fwd_gather")
+
+
+def sa_predict_mask_gather_noalloc(q, k, perm, p: SaMaskParams, row_ptr, col_idx, dev_status, mask_out=None,
+                                   sim_q=None, sim_k=None, stream=None):
+    """sa_predict_mask_gather with the library's fixed per-GPU workspace (allocates nothing)."""
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(perm, "perm", "int32"),
+          _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"), _a(dev_status, "dev_status", "int32"),
+          _a(mask_out, "mask_out", "uint8", optional=True), _a(sim_q, "sim_q", "float32", optional=True),
+          _a(sim_k, "sim_k", "float32", optional=True))
+    code = lib().sa_predict_mask_gather_noalloc(_ptr(q), _ptr(k), _ptr(perm), ctypes.byref(p), _ptr(row_ptr),
+                                                _ptr(col_idx), col_idx.numel(), _ptr(mask_out), _ptr(sim_q),
+                                                _ptr(sim_k), _ptr(dev_status), _stream(stream))
+    _check(code, "sa_predict_mask_gather_noalloc")

@@ -149,9 +149,9 @@ extern "C" int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off
     return SA_OK;
 }
 
-namespace {
+namespace sa {
 
-int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
+int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
                  const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                  int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status,
                  void* stream) {
@@ -210,6 +210,10 @@ int predict_mask(const uint16_t* q, const uint16_t* k, const int32_t* perm, cons
     return SA_OK;
 }
 
+}  // namespace sa
+
+namespace {
+
 int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* perm, float* o,
                     const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
                     int64_t* counters, int32_t* dev_status, void* stream) {
@@ -244,7 +248,7 @@ extern "C" int sa_predict_mask(const uint16_t* q, const uint16_t* k, const sa_ma
                                void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
                                int32_t* dev_status, void* stream) {
-    return predict_mask(q, k, nullptr, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+    return predict_mask_impl(q, k, nullptr, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
                         dev_status, stream);
 }
 
@@ -253,7 +257,7 @@ extern "C" int sa_predict_mask_gather(const uint16_t* q, const uint16_t* k, cons
                                       int32_t* col_idx, int64_t col_cap, uint8_t* mask_out, float* sim_q,
                                       float* sim_k, int32_t* dev_status, void* stream) {
     if (!perm_dev) return SA_ERR_INVALID_ARGUMENT;
-    return predict_mask(q, k, perm_dev, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
+    return predict_mask_impl(q, k, perm_dev, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out, sim_q, sim_k,
                         dev_status, stream);
 }
 
@@ -261,7 +265,7 @@ extern "C" int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const in
                                   const uint8_t* forced_dev, const sa_mask_params* p, void* ws, size_t ws_bytes,
                                   int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, uint8_t* mask_out,
                                   float* sim_q, float* sim_k, int32_t* dev_status, void* stream) {
-    return predict_mask(q, k, perm_dev, forced_dev, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out,
+    return predict_mask_impl(q, k, perm_dev, forced_dev, p, ws, ws_bytes, row_ptr, col_idx, col_cap, mask_out,
                         sim_q, sim_k, dev_status, stream);
 }
 

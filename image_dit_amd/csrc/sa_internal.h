@@ -92,4 +92,11 @@ struct FlashArgs {
 
 hipError_t launch_flash(const FlashArgs& a, hipStream_t stream);
 
+// The body of the sa_predict_mask* entry points: argument checks, workspace
+// carving and the three prediction launches (perm, forced: optional).
+int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
+                      const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
+                      int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status,
+                      void* stream);
+
 }  // namespace sa

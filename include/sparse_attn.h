@@ -286,6 +286,27 @@ int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const int32_t* perm
                        int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, uint8_t* mask_out,
                        float* sim_q, float* sim_k, int32_t* dev_status, void* stream);
 
+/* Bytes of the fixed device workspace of sa_predict_mask_gather_noalloc
+ * (64 MiB, one copy per GPU for the life of the process). */
+#define SA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sa_predict_mask_gather without the ws/ws_bytes arguments.  The workspace is
+ * a fixed SA_NOALLOC_SCRATCH_BYTES device array inside this library (one per
+ * GPU, kept until the process ends); the call allocates nothing.  Parameters
+ * whose sa_predict_workspace_bytes exceeds SA_NOALLOC_SCRATCH_BYTES are refused
+ * with SA_ERR_CAPACITY before anything is enqueued.  All calls on one GPU share
+ * that GPU's array: calls that may run at the same time on one GPU (different
+ * streams without ordering) race and must not be issued; calls ordered on one
+ * stream are safe.  The first call on a device looks the array's address up
+ * (a HIP runtime query, no allocation); a failure there returns SA_ERR_HIP.
+ * Outputs, errors and the other arguments as in sa_predict_mask_gather. */
+int sa_predict_mask_gather_noalloc(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                                   const sa_mask_params* p, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k,
+                                   int32_t* dev_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

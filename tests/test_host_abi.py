@@ -377,3 +377,21 @@ def test_binding_refuses_tensors_the_abi_would_misread():
         sa.sa_sparse_attn_fwd(y.half(), y, y, o, p, rp, rp, st)
     with pytest.raises(TypeError):
         sa.sa_sparse_attn_fwd(y, y, y, o, p, rp.long(), rp, st)
+
+
+def test_noalloc_prediction_refuses_workspaces_over_its_array():
+    """The allocation-free prediction entry refuses, before touching the GPU, parameters
+    whose workspace exceeds its fixed per-GPU array, and rejects invalid ones as usual."""
+    big = sa.make_mask_params(1, 64, 64, 131072, 128, 128, 64, tau=0.9)
+    assert sa.sa_predict_workspace_bytes(big) > sa.SA_NOALLOC_SCRATCH_BYTES
+    L = sa.lib()
+    fake = ctypes.c_void_p(256)  # never dereferenced: the size check comes first
+    args = (fake, fake, fake)
+    rc = L.sa_predict_mask_gather_noalloc(*args, ctypes.byref(big), fake, fake, 0, None, None, None, fake, None)
+    assert rc == sa.SA_ERR_CAPACITY
+    bad = sa.make_mask_params(1, 2, 2, 1000, 96, 128, 64, tau=0.9)  # head dim not compiled
+    rc = L.sa_predict_mask_gather_noalloc(*args, ctypes.byref(bad), fake, fake, 0, None, None, None, fake, None)
+    assert rc == sa.SA_ERR_UNSUPPORTED
+    rc = L.sa_predict_mask_gather_noalloc(fake, fake, None, ctypes.byref(big), fake, fake, 0, None, None, None,
+                                          fake, None)
+    assert rc == sa.SA_ERR_INVALID_ARGUMENT
