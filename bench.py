@@ -20,6 +20,9 @@ workload (rank 0, N=1 only).
 
 Extra modes (not the benchmark line):
   --mode attn      only the sparse attention launch, repeated (for rocprofv3 counters)
+  --mode predict   only the mask prediction launch, repeated (for rocprofv3 counters)
+  --mode reorder   only the reorder copies of the materialising form (three permutes and
+                   the un-permute), repeated (for rocprofv3 counters)
   --mode copy      a plain device copy of known size (HBM counter calibration)
   --mode ceilings  what the box reaches outside this library: a bf16 GEMM through torch
                    (hipBLASLt) and torch's dense flash attention at the workload's shape
@@ -50,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
-    ap.add_argument("--mode", default="path", choices=["path", "attn", "copy", "ceilings"])
+    ap.add_argument("--mode", default="path", choices=["path", "attn", "predict", "reorder", "copy", "ceilings"])
     ap.add_argument("--no-lambda", action="store_true", help="turn the workload's PV skip off")
     ap.add_argument("--form", default="gather", choices=["gather", "materialize"],
                     help="reorder inside the kernels' loads (bf16 inputs) or as separate copies")
@@ -101,14 +104,28 @@ def executed_flops(cfg, rp, ci, skip, groups):
     return qk, pv
 
 
-def cpu_baseline(w, path, q, k, v, budget_s):
-    """Oracle on a bounded sample: prediction of one head + attention of the first query blocks."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo", encoding="utf8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, path, q, k, v, budget_s, gmask0=None):
+    """Oracle on a bounded sample: prediction of one head + attention of the first query blocks.
+    With gmask0 (the library's mask rows of head 0) the oracle's rows of that head are also
+    compared with it (admissible rows, borderline counts)."""
     import numpy as np
 
     from oracle import flash as OF
     from oracle import layout as OL
     from oracle import numerics as ON
     from oracle import predict as OP
+    from oracle.admissible import borderline_counts, compare_head_mask
 
     try:
         from threadpoolctl import threadpool_info
@@ -125,9 +142,16 @@ def cpu_baseline(w, path, q, k, v, budget_s):
                        sink_front=w.sink_front, sink_back=w.sink_back, tau=w.tau, theta=w.theta,
                        sparsity=cfg.sparsity, sink_rows=w.sink_rows)
     t0 = time.perf_counter()
-    OP.predict_head(qp, kp, mp)
+    ref = OP.predict_head(qp, kp, mp)
     t_pred = time.perf_counter() - t0
+    mask_check = None
+    if gmask0 is not None:
+        bad, differ, checked, kinds = compare_head_mask(gmask0, ref, mp)
+        mask_check = {"head": 0, "rows": checked, "not_admissible": len(bad), "differing_borderline": len(differ),
+                      "differing_by_kind": kinds, "flagged_borderline": borderline_counts(ref)}
     rp, ci = path.csr_host()
+    skip_gpu = path.pv_skip.cpu().numpy() if (path.pv_skip is not None and w.lam is not None) else None
+    lam_stats = {"decisions": 0, "near_border": 0, "differ": 0, "differ_outside_border": 0}
     t0 = time.perf_counter()
     flops = 0.0
     nblk = 0
@@ -135,6 +159,16 @@ def cpu_baseline(w, path, q, k, v, budget_s):
         cols = ci[rp[nblk]:rp[nblk + 1]]
         _, rec = OF.attend_qblock(qp, kp, vp, nblk, cols, w.block_q, w.block_k, causal=w.causal,
                                   lam=w.lam if w.lam is not None else None)
+        if skip_gpu is not None:
+            ng = rec["skip"].shape[1]
+            gpu = np.array([[bool(skip_gpu[(rp[nblk] + e) * path.groups + g]) for g in range(ng)]
+                            for e in range(len(cols))], dtype=bool).reshape(len(cols), ng)
+            near = np.abs(rec["gap"] - w.lam) <= 1e-3
+            diff = gpu != rec["skip"]
+            lam_stats["decisions"] += int(gpu.size)
+            lam_stats["near_border"] += int(near.sum())
+            lam_stats["differ"] += int(diff.sum())
+            lam_stats["differ_outside_border"] += int((diff & ~near).sum())
         rows = min((nblk + 1) * w.block_q, w.N) - nblk * w.block_q
         kts = np.array([min((j + 1) * w.block_k, w.N) - j * w.block_k for j in cols], dtype=np.float64)
         flops += 2.0 * rows * kts.sum() * w.D  # QK
@@ -146,10 +180,18 @@ def cpu_baseline(w, path, q, k, v, budget_s):
     # per-head prediction cost is shared by the head's n_qb query blocks
     t_pred_share = t_pred * nblk / cfg.n_qb
     value = flops / (t_attn + t_pred_share) / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"head 0: block stats + mask prediction of all {cfg.n_qb} query blocks "
-                       f"({t_pred:.2f} s, charged pro rata) and fp64 attention with PV-skip emulation "
-                       f"on the first {nblk} query blocks over the GPU's CSR ({t_attn:.2f} s)")}
+    out = {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"head 0: block stats + mask prediction of all {cfg.n_qb} query blocks "
+                      f"({t_pred:.2f} s, charged pro rata) and fp64 attention with PV-skip emulation "
+                      f"on the first {nblk} query blocks over the GPU's CSR ({t_attn:.2f} s)"),
+           "threads": int(threads), "host_cpus": os.cpu_count(), "model": cpu_model(),
+           "thread_setting": f"NumPy BLAS threads as the environment sets them (OMP_NUM_THREADS="
+                             f"{os.environ.get('OMP_NUM_THREADS', 'unset')})"}
+    if mask_check is not None:
+        out["mask_check"] = mask_check
+    if skip_gpu is not None:
+        out["mask_check"] = dict(out.get("mask_check", {}), lambda_decisions=lam_stats)
+    return out
 
 
 def _event_ms(torch, f, reps):
@@ -254,13 +296,22 @@ def main():
         for _, f in stages:
             f()
 
-    if args.mode == "attn":
+    if args.mode in ("attn", "predict"):
         run_step()
         for _ in range(max(1, args.steps)):
-            stages[2][1]()
+            stages[2 if args.mode == "attn" else 1][1]()
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "attn", "form": "gather" if gather else "materialize",
+        print(json.dumps({"mode": args.mode, "form": "gather" if gather else "materialize",
                           "launches": max(1, args.steps) + 1}))
+        return
+    if args.mode == "reorder":
+        if gather:
+            path = sa.SparseAttentionPath(cfg, materialize=True)
+        for _ in range(max(1, args.steps)):
+            path.permute(qd, kd, vd)
+            path.unpermute()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "reorder", "launches": max(1, args.steps)}))
         return
 
     stream = torch.cuda.current_stream()
@@ -387,7 +438,17 @@ def main():
         "gen_s": round(t_gen, 1),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, path, q, k, v, args.cpu_seconds)
+        # the library's mask rows of head 0, for the oracle's row-by-row check (after timing)
+        mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
+        if gather:
+            path.predict_gather(qd, kd, mask_out=mask)
+        else:
+            path.permute(qd, kd, vd)
+            path.predict(mask_out=mask)
+        torch.cuda.synchronize()
+        gmask0 = mask[:cfg.n_qb].cpu().numpy().astype(bool)
+        out["cpu_baseline"] = cpu_baseline(w, path, q, k, v, args.cpu_seconds, gmask0)
+        out["borderline"] = out["cpu_baseline"].pop("mask_check", None)
     print(json.dumps(out), flush=True)
 
 

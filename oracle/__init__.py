@@ -24,6 +24,8 @@ What is computed, and where on the pages it comes from:
   PV-skip emulation in the online-softmax recurrence (SpargeAttn notes,
   sections 2.1 and 2.3).
 * ``numerics``   -- exact bf16 upcast and float32 -> bf16 round-to-nearest-even.
+* ``admissible`` -- which mask rows the predictor's reading admits when a
+  decision lies within rounding of its threshold (used by the parity checks).
 
 Every function is pinned by a ``-m "not gpu"`` test against values printed on
 the pages, closed forms, brute force or textbook special cases.  The quality
@@ -31,4 +33,4 @@ of the predicted mask against dense attention (relative L1, MSE) is reported
 but **parity unpinned**: the pages' quality figures come from real models.
 """
 
-from . import attention, flash, layout, numerics, predict  # noqa: F401
+from . import admissible, attention, flash, layout, numerics, predict  # noqa: F401
