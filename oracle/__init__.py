@@ -24,6 +24,9 @@ What is computed, and where on the pages it comes from:
   PV-skip emulation in the online-softmax recurrence (SpargeAttn notes,
   sections 2.1 and 2.3).
 * ``numerics``   -- exact bf16 upcast and float32 -> bf16 round-to-nearest-even.
+* ``quant``      -- per-block 8-bit (OCP FP8 E4M3) quantization of the QK
+  operands with one dequantization scale per block (SpargeAttn notes,
+  section 2.4), written from the format's definition.
 * ``admissible`` -- which mask rows the predictor's reading admits when a
   decision lies within rounding of its threshold (used by the parity checks).
 
@@ -33,4 +36,4 @@ of the predicted mask against dense attention (relative L1, MSE) is reported
 but **parity unpinned**: the pages' quality figures come from real models.
 """
 
-from . import admissible, attention, flash, layout, numerics, predict  # noqa: F401
+from . import admissible, attention, flash, layout, numerics, predict, quant  # noqa: F401
