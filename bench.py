@@ -18,6 +18,11 @@ Prints ONE JSON line.  ``value`` is executed TFLOP/s of the whole step
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload (rank 0, N=1 only).
 
+``--qk fp8`` times the FP8 QK variant instead (Q and K quantized to per-block
+E4M3 codes inside each step, QK products on the fp8 matrix cores, P V in
+bf16); its roofline peak is the time-weighted mix of the fp8 and bf16 peaks
+over its QK and PV flops, and it has no oracle leg.
+
 Extra modes (not the benchmark line):
   --mode attn      only the sparse attention launch, repeated (for rocprofv3 counters)
   --mode predict   only the mask prediction launch, repeated (for rocprofv3 counters)
@@ -41,6 +46,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "block-sparse attn fwd: ms/call + executed TFLOP/s (MFMA %) at sparsity 0.8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_traffic_long_video.json")
@@ -57,6 +63,8 @@ def parse():
     ap.add_argument("--no-lambda", action="store_true", help="turn the workload's PV skip off")
     ap.add_argument("--form", default="gather", choices=["gather", "materialize"],
                     help="reorder inside the kernels' loads (bf16 inputs) or as separate copies")
+    ap.add_argument("--qk", default="bf16", choices=["bf16", "fp8"],
+                    help="QK products on bf16 operands, or on per-block E4M3 codes (quantized inside the step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
@@ -70,16 +78,17 @@ def flash_source_hash():
     return h.hexdigest()[:16]
 
 
-def attn_kernel_name(cfg, gather):
+def attn_kernel_name(cfg, gather, fp8=False):
     """The attention kernel the attention entry point launches for this configuration."""
     if cfg.block_q == 16 and cfg.block_k == 16:
         return "k_flash_small"
     if cfg.lam is not None and cfg.block_k == 128:
         return "k_flash_mfma"
     g = "true" if gather else "false"
+    f = "true" if fp8 else "false"
     if cfg.lam is not None:
-        return f"k_flash_lam<{cfg.D}, {g}>"
-    return f"k_flash_dma<{cfg.D}, {1 if cfg.block_k == 64 else 2}, {g}>"
+        return f"k_flash_lam<{cfg.D}, {g}, {f}>"
+    return f"k_flash_dma<{cfg.D}, {1 if cfg.block_k == 64 else 2}, {g}, {f}>"
 
 
 def executed_flops(cfg, rp, ci, skip, groups):
@@ -271,7 +280,8 @@ def main():
         return
     cfg = sa.config_from_workload(w)
     gather = args.form == "gather" and w.dtype == "bf16"
-    path = sa.SparseAttentionPath(cfg, materialize=not gather)
+    fp8 = args.qk == "fp8"
+    path = sa.SparseAttentionPath(cfg, materialize=not gather, qk_fp8=fp8)
     t_gen = time.perf_counter()
     q, k, v = generate(w)
     t_gen = time.perf_counter() - t_gen
@@ -284,13 +294,25 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     torch.cuda.synchronize()
 
-    # the step's stages; the gather form has no separate reorder copies
+    # the step's stages; the gather form has no separate reorder copies; the FP8 QK
+    # path quantizes Q and K (its own stage) before the attention
     if gather:
-        stages = [("permute", lambda: None), ("predict", lambda: path.predict_gather(qd, kd)),
-                  ("attn", lambda: path.attend_gather(qd, kd, vd)), ("unpermute", lambda: None)]
+        stages = [("permute", lambda: None), ("predict", lambda: path.predict_gather(qd, kd))]
+        if fp8:
+            stages += [("quantize", lambda: path.quantize(qd, kd, path.perm, path.perm)),
+                       ("attn", lambda: path.attend_qk8_gather(vd))]
+        else:
+            stages += [("attn", lambda: path.attend_gather(qd, kd, vd))]
+        stages += [("unpermute", lambda: None)]
     else:
-        stages = [("permute", lambda: path.permute(qd, kd, vd)), ("predict", path.predict),
-                  ("attn", path.attend), ("unpermute", path.unpermute)]
+        stages = [("permute", lambda: path.permute(qd, kd, vd)), ("predict", path.predict)]
+        if fp8:
+            stages += [("quantize", lambda: path.quantize(path.qp, path.kp)),
+                       ("attn", path.attend_qk8)]
+        else:
+            stages += [("attn", path.attend)]
+        stages += [("unpermute", path.unpermute)]
+    idx = {name: j for j, (name, _) in enumerate(stages)}
 
     def run_step():
         for _, f in stages:
@@ -299,7 +321,7 @@ def main():
     if args.mode in ("attn", "predict"):
         run_step()
         for _ in range(max(1, args.steps)):
-            stages[2 if args.mode == "attn" else 1][1]()
+            stages[idx[args.mode]][1]()
         torch.cuda.synchronize()
         print(json.dumps({"mode": args.mode, "form": "gather" if gather else "materialize",
                           "launches": max(1, args.steps) + 1}))
@@ -338,7 +360,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = ev[0][0].elapsed_time(end)
-    stage = np.zeros(4)
+    stage = np.zeros(len(stages))
     for s in range(K):
         for x, j in enumerate(real):
             nxt = ev[s][x + 1] if x + 1 < len(real) else (ev[s + 1][0] if s + 1 < K else end)
@@ -367,14 +389,19 @@ def main():
     pv_groups_total = cnt[1] + cnt[2]
     combined = 1.0 - (nnz + cnt[1] * (nnz / max(1, pv_groups_total))) / (2.0 * valid_blocks.sum())
 
-    attn_ms = stage[2]
+    attn_ms = stage[idx["attn"]]
     attn_tflops = exec_flops / (attn_ms * 1e-3) / 1e12
+    # the attention kernel's MFMA peak: bf16, or (FP8 QK) the time-weighted mix of the
+    # fp8 QK and bf16 PV peaks
+    peak = PEAK_BF16_TFLOPS if not fp8 else exec_flops / (qk / PEAK_FP8_TFLOPS + pv / PEAK_BF16_TFLOPS)
     n_qb, n_kb = cfg.n_qb, cfg.n_kb
     pred_bytes = (2 * (B * Hq * N * d + B * Hkv * N * d) + 4 * (B * Hq * n_qb + B * Hkv * n_kb) * d
                   + 4 * (B * Hq * n_qb + B * Hkv * n_kb) + 2 * B * Hq * n_qb * n_kb
                   + 4 * (B * Hq * n_qb + 1) + 4 * nnz + (4 * N if gather else 0))
     perm_bytes = (B * Hq * N * d + 2 * B * Hkv * N * d) * ((4 if w.dtype == "f32" else 2) + 2)
     unperm_bytes = 2 * 4 * B * Hq * N * d
+    # quantize: Q and K read (bf16) and written (one byte per element), plus the scales
+    quant_bytes = 3 * (B * Hq * N * d + B * Hkv * N * d) + 4 * (B * Hq * n_qb + B * Hkv * -(-N // 64))
 
     traffic = None
     try:
@@ -382,7 +409,8 @@ def main():
             tr = json.load(f)
         if tr.get("source_sha") == flash_source_hash() and tr.get("workload") == args.workload \
                 and abs(tr.get("sparsity", -1) - (cfg.sparsity or 0)) < 1e-9 \
-                and tr.get("form", "materialize") == ("gather" if gather else "materialize"):
+                and tr.get("form", "materialize") == ("gather" if gather else "materialize") \
+                and tr.get("qk", "bf16") == args.qk:
             traffic = tr["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -398,7 +426,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 (QK) + bf16 (PV)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": (f"{w.name}: B{B} Hq{Hq} Hkv{Hkv} latent{list(w.latent)} txt{w.txt_len} N{N} d{d} "
@@ -407,37 +435,41 @@ def main():
             "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "block_q": cfg.block_q, "block_k": cfg.block_k,
             "sparsity_target": cfg.sparsity,
             "reorder": "gather (inside the kernels' loads)" if gather else "materialized copies",
+            "qk": "fp8 e4m3, one scale per 128-row query block and per 64-key tile" if fp8 else "bf16",
         },
-        "ms": ({"predict": round(stage[1], 4), "attn": round(attn_ms, 4)} if gather else
-               {"permute": round(stage[0], 4), "predict": round(stage[1], 4), "attn": round(attn_ms, 4),
-                "unpermute": round(stage[3], 4)}),
+        "ms": {name: round(stage[j], 4) for name, j in idx.items()
+               if not (gather and name in ("permute", "unpermute"))},
         "attn_executed_tflops": round(attn_tflops, 2),
-        "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_mfma_frac": round(attn_tflops / peak, 4),
         "dense_equiv_tflops_step": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
-        "dense_equiv_tflops_attn_plus_predict": round(dense_flops / ((attn_ms + stage[1]) * 1e-3) / 1e12, 2),
+        "dense_equiv_tflops_attn_plus_predict": round(
+            dense_flops / ((attn_ms + stage[idx["predict"]] + (stage[idx["quantize"]] if fp8 else 0.0)) * 1e-3)
+            / 1e12, 2),
         "executed_tflop": round(exec_flops / 1e12, 4),
         "dense_tflop": round(dense_flops / 1e12, 4),
         "mask_sparsity": round(mask_sparsity, 4),
         "combined_qk_pv_sparsity": round(float(combined), 4),
         "pv_group_blocks": {"executed": int(cnt[1]), "skipped": int(cnt[2])},
-        "predict_gbs": round(pred_bytes / (stage[1] * 1e-3) / 1e9, 1),
-        "predict_hbm_frac": round(pred_bytes / (stage[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        **({} if gather else {"permute_gbs": round(perm_bytes / (stage[0] * 1e-3) / 1e9, 1),
-                              "unpermute_gbs": round(unperm_bytes / (stage[3] * 1e-3) / 1e9, 1)}),
+        "predict_gbs": round(pred_bytes / (stage[idx["predict"]] * 1e-3) / 1e9, 1),
+        "predict_hbm_frac": round(pred_bytes / (stage[idx["predict"]] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        **({} if gather else {"permute_gbs": round(perm_bytes / (stage[idx["permute"]] * 1e-3) / 1e9, 1),
+                              "unpermute_gbs": round(unperm_bytes / (stage[idx["unpermute"]] * 1e-3) / 1e9, 1)}),
+        **({} if not fp8 else {"quantize_gbs": round(quant_bytes / (stage[idx["quantize"]] * 1e-3) / 1e9, 1)}),
         "roofline": {
             "bound": "mfma",
-            "kernel": attn_kernel_name(cfg, gather) + " (+ k_attn_init), per "
-                      + ("sa_sparse_attn_fwd_gather" if gather else "sa_sparse_attn_fwd") + " call",
+            "kernel": attn_kernel_name(cfg, gather, fp8) + " (+ k_attn_init), per "
+                      + ("sa_sparse_attn_fwd_qk8" if fp8 else
+                         "sa_sparse_attn_fwd_gather" if gather else "sa_sparse_attn_fwd") + " call",
             "achieved": round(attn_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": round(peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(attn_tflops / peak, 4),
             "traffic": traffic,
         },
         "wall_s_timed": round(t_wall, 3),
         "gen_s": round(t_gen, 1),
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not fp8:  # (the oracle sample follows the bf16 path)
         # the library's mask rows of head 0, for the oracle's row-by-row check (after timing)
         mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
         if gather:

@@ -26,11 +26,13 @@ SA_ORDER_HILBERT = 2
 SA_PV_GROUP_ROWS = 32
 SA_MAX_KEY_BLOCKS = 2048
 SA_NOALLOC_SCRATCH_BYTES = 64 << 20
+SA_FP8_KEY_ROWS = 64
 
 EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermute",
            "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
            "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather",
-           "sa_plan_tile_window", "sa_predict_mask_ex", "sa_predict_mask_gather_noalloc")
+           "sa_plan_tile_window", "sa_predict_mask_ex", "sa_predict_mask_gather_noalloc",
+           "sa_quantize_fp8", "sa_sparse_attn_fwd_qk8")
 
 
 class SaLayout(ctypes.Structure):
@@ -106,6 +108,13 @@ def lib() -> ctypes.CDLL:
                                                  c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                                  c_void_p]
     L.sa_predict_mask_gather_noalloc.restype = c_int
+    L.sa_quantize_fp8.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_int32, c_int32, c_void_p,
+                                  c_void_p, c_void_p]
+    L.sa_quantize_fp8.restype = c_int
+    L.sa_sparse_attn_fwd_qk8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         POINTER(SaAttnParams), c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]
+    L.sa_sparse_attn_fwd_qk8.restype = c_int
     _lib = L
     return L
 
@@ -307,3 +316,34 @@ def sa_predict_mask_gather_noalloc(q, k, perm, p: SaMaskParams, row_ptr, col_idx
                                                 _ptr(col_idx), col_idx.numel(), _ptr(mask_out), _ptr(sim_q),
                                                 _ptr(sim_k), _ptr(dev_status), _stream(stream))
     _check(code, "sa_predict_mask_gather_noalloc")
+
+
+def sa_quantize_fp8(x, perm, block, codes, scales, stream=None):
+    """Per-block E4M3 codes and scales of x (bf16 [B, H, N, D], original order); blocks of
+    `block` rows of the order perm gives (None: identity)."""
+    _need(_a(x, "x", "bfloat16"), _a(perm, "perm", "int32", optional=True), _a(codes, "codes", "uint8"),
+          _a(scales, "scales", "float32"))
+    if x.dim() != 4 or tuple(codes.shape) != tuple(x.shape):
+        raise ValueError("x must be [B, H, N, D] and codes of the same shape")
+    B, H, N, D = x.shape
+    nb = -(-N // block)
+    if scales.numel() != B * H * nb:
+        raise ValueError(f"scales must hold B*H*ceil(N/block) = {B * H * nb} entries")
+    code = lib().sa_quantize_fp8(_ptr(x), _ptr(perm), B, H, N, D, block, _ptr(codes), _ptr(scales),
+                                 _stream(stream))
+    _check(code, "sa_quantize_fp8")
+
+
+def sa_sparse_attn_fwd_qk8(q8, q_scale, k8, k_scale, v, perm, o, p: SaAttnParams, row_ptr, col_idx, dev_status,
+                           pv_skip=None, counters=None, stream=None):
+    """sparse attention with FP8 QK operands (codes and scales from sa_quantize_fp8); perm None:
+    everything in the reordered order, else as sa_sparse_attn_fwd_gather."""
+    _need(_a(q8, "q8", "uint8"), _a(q_scale, "q_scale", "float32"), _a(k8, "k8", "uint8"),
+          _a(k_scale, "k_scale", "float32"), _a(v, "v", "bfloat16"), _a(perm, "perm", "int32", optional=True),
+          _a(o, "o", "float32"), _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"),
+          _a(dev_status, "dev_status", "int32"), _a(pv_skip, "pv_skip", "uint8", optional=True),
+          _a(counters, "counters", "int64", optional=True))
+    code = lib().sa_sparse_attn_fwd_qk8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(perm),
+                                        _ptr(o), ctypes.byref(p), _ptr(row_ptr), _ptr(col_idx), _ptr(pv_skip),
+                                        _ptr(counters), _ptr(dev_status), _stream(stream))
+    _check(code, "sa_sparse_attn_fwd_qk8")

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libsparse_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "planner.cpp", "permute.hip", "predict.hip", "flash.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "permute.hip", "predict.hip", "flash.hip", "noalloc.hip", "quant.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -214,17 +214,40 @@ int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm,
 
 namespace {
 
+// FP8 QK operands of sa_sparse_attn_fwd_qk8 (all null on the bf16 path)
+struct QK8 {
+    const uint8_t* q8 = nullptr;
+    const float* q_scale = nullptr;
+    const uint8_t* k8 = nullptr;
+    const float* k_scale = nullptr;
+};
+
 int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* perm, float* o,
                     const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx, uint8_t* pv_skip,
-                    int64_t* counters, int32_t* dev_status, void* stream) {
+                    int64_t* counters, int32_t* dev_status, void* stream, const QK8& f8 = QK8{}) {
     const int st = validate_attn(p);
     if (st != SA_OK) return st;
-    if (!q || !k || !v || !o || !row_ptr || !col_idx || !dev_status) return SA_ERR_INVALID_ARGUMENT;
+    const bool fp8 = f8.q8 != nullptr;
+    if (fp8) {
+        if (!f8.k8 || !f8.q_scale || !f8.k_scale) return SA_ERR_INVALID_ARGUMENT;
+        if ((reinterpret_cast<uintptr_t>(f8.q8) | reinterpret_cast<uintptr_t>(f8.k8)) & 15 ||
+            (reinterpret_cast<uintptr_t>(f8.q_scale) | reinterpret_cast<uintptr_t>(f8.k_scale)) & 3)
+            return SA_ERR_INVALID_ARGUMENT;
+        const int64_t nk = p->n_keys > 0 ? p->n_keys : p->N;
+        if (p->D != 128 || p->block_q != 128 || !(p->block_k == 64 || (p->block_k == 128 && !(p->lambda > -INFINITY))))
+            return SA_ERR_UNSUPPORTED;
+        if ((nk + kKeyQuantRows - 1) / kKeyQuantRows >= kMaxKeyTiles) return SA_ERR_UNSUPPORTED;
+        q = k = nullptr;
+    } else if (!q || !k) {
+        return SA_ERR_INVALID_ARGUMENT;
+    }
+    if (!v || !o || !row_ptr || !col_idx || !dev_status) return SA_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
          reinterpret_cast<uintptr_t>(o)) & 15)
         return SA_ERR_INVALID_ARGUMENT;
     FlashArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
+    a.q8 = f8.q8; a.k8 = f8.k8; a.q_scale = f8.q_scale; a.k_scale = f8.k_scale;
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.perm = perm; a.pv_skip = pv_skip;
     a.counters = reinterpret_cast<unsigned long long*>(counters);
     a.dev_status = dev_status;
@@ -234,6 +257,7 @@ int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     a.bq = p->block_q; a.bk = p->block_k;
     a.n_qb = int((p->N + p->block_q - 1) / p->block_q);
     a.n_kb = int((a.Nk + p->block_k - 1) / p->block_k);
+    a.n_kt = int((a.Nk + kKeyQuantRows - 1) / kKeyQuantRows);
     a.col_cap = p->col_cap;
     a.causal = p->causal;
     a.lambda = p->lambda;
@@ -282,4 +306,28 @@ extern "C" int sa_sparse_attn_fwd_gather(const uint16_t* q, const uint16_t* k, c
                                          int64_t* counters, int32_t* dev_status, void* stream) {
     if (!perm_dev) return SA_ERR_INVALID_ARGUMENT;
     return sparse_attn_fwd(q, k, v, perm_dev, o, p, row_ptr, col_idx, pv_skip, counters, dev_status, stream);
+}
+
+extern "C" int sa_quantize_fp8(const uint16_t* x, const int32_t* perm_dev, int32_t B, int32_t H, int64_t N,
+                               int32_t D, int32_t block, uint8_t* codes, float* scales, void* stream) {
+    if (!x || !codes || !scales || B <= 0 || H <= 0 || N <= 0 || N > INT32_MAX) return SA_ERR_INVALID_ARGUMENT;
+    if (block <= 0 || block > kQuantMaxBlock) return SA_ERR_INVALID_ARGUMENT;
+    if (!head_dim_ok(D)) return SA_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 7) ||
+        (reinterpret_cast<uintptr_t>(scales) & 3))
+        return SA_ERR_INVALID_ARGUMENT;
+    const hipError_t e = launch_quant_fp8(x, perm_dev, int64_t(B) * H, N, D, block, codes, scales,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+extern "C" int sa_sparse_attn_fwd_qk8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                      const float* k_scale, const uint16_t* v, const int32_t* perm_dev, float* o,
+                                      const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
+                                      uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream) {
+    if (!q8) return SA_ERR_INVALID_ARGUMENT;
+    QK8 f8;
+    f8.q8 = q8; f8.q_scale = q_scale; f8.k8 = k8; f8.k_scale = k_scale;
+    return sparse_attn_fwd(nullptr, nullptr, v, perm_dev, o, p, row_ptr, col_idx, pv_skip, counters, dev_status,
+                           stream, f8);
 }

@@ -45,6 +45,17 @@ __device__ inline float wave_max(float v) {
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// 32 E4M3 codes per lane: the A/B operand of v_mfma_f32_32x32x64_f8f6f4
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ inline i32x8 cat8(uint4 a, uint4 b) {
+    return i32x8{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
+}
+// C += A B over 64 products per element, both operands E4M3 (format code 0);
+// with no block scales the compiler emits the unscaled instruction
+__device__ inline floatx16 mfma_fp8(i32x8 a, i32x8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -388,6 +399,51 @@ __device__ inline void q_ready(const bf16x8_t (&qf)[KS]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qf[ks]));
 }
+// (in 128-bit halves: a wider asm operand silently voids the kernel's host
+// launch stub)
+template <int KS>
+__device__ inline void q_ready(const i32x8 (&qf)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qf[ks].lo), "v"(qf[ks].hi));
+}
+
+// FP8 QK operands (D = 128): a query row is 128 bytes of E4M3 codes, so a
+// 64-key K tile is 8 KB in LDS, laid out like a bf16 tile of head dim 64: 8-row
+// lines of 128-byte rows, 16-byte chunk p of row r holding source chunk
+// p ^ ((r >> 1) & 7).  For k-step ks (64 head-dim entries) lane l supplies
+// entries 64 ks + 32 (l >> 5) .. +31 of its key row (A operand) or query row
+// (B operand), so both operands agree on which products are summed.
+// Q codes of this lane's query row, two k-steps
+__device__ inline void load_q8(const uint8_t* q8_head, uint32_t head_bytes, int qsrc, int half, i32x8 (&qf)[2]) {
+    const __amdgpu_buffer_rsrc_t rQ = head_rsrc(q8_head, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t off = uint32_t(qsrc) * 128u + uint32_t(64 * ks + 32 * half);
+        qf[ks] = cat8(bload16(rQ, off), bload16(rQ, off + 16u));
+    }
+}
+// byte offsets of this lane's four 16-byte K operand chunks in an FP8 tile:
+// [2 ks + x] = chunk 4 ks + 2 half + x of key row l32 (add 4096 for rows 32..63)
+__device__ inline void k8_offsets(int l32, int half, int (&off)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            off[2 * ks + x] = (l32 >> 3) * 1024 + (l32 & 7) * 128 + (((4 * ks + 2 * half + x) ^ ((l32 >> 1) & 7)) * 16);
+}
+// raw scores of a 64-key FP8 tile: s0 keys 0..31, s1 keys 32..63 (code units)
+__device__ inline void qk_fp8(const uint8_t* K8, const int (&off)[4], const i32x8 (&qf)[2], floatx16& s0,
+                              floatx16& s1) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint8_t* p = K8 + off[2 * ks];
+        const uint8_t* p1 = K8 + off[2 * ks + 1];
+        const i32x8 a0 = cat8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p1));
+        const i32x8 a1 = cat8(*reinterpret_cast<const uint4*>(p + 4096), *reinterpret_cast<const uint4*>(p1 + 4096));
+        s0 = mfma_fp8(a0, qf[ks], s0);
+        s1 = mfma_fp8(a1, qf[ks], s1);
+    }
+}
 // vmcnt(N): at most N of this wave's vector memory operations outstanding
 template <int N>
 __device__ inline void dma_wait() {
@@ -428,7 +484,7 @@ struct TileLane {
 
 // lambda off: every kept tile runs its PV product.  K and V run one tile
 // ahead in two LDS buffers each.  128-key blocks run as two 64-key tiles.
-template <int D, int SUB, bool GATHER>
+template <int D, int SUB, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                  uint8_t* __restrict__ pv_skip) {
@@ -438,13 +494,16 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int KS = D / 16;               // MFMA k-steps over the head dim
     constexpr int SEG = D / 64;              // 128-byte segments per row
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
+    static_assert(!FP8 || D == 128, "the FP8 QK path has head dim 128");
+    constexpr int KT = FP8 ? BK * D / 2 : BK * D;  // uint16 slots of one K tile
     // One array per buffer, selected at compile time, so that operand reads
     // use constant LDS addresses.
-    __shared__ __align__(16) uint16_t Ks0[BK * D];
-    __shared__ __align__(16) uint16_t Ks1[BK * D];
+    __shared__ __align__(16) uint16_t Ks0[KT];
+    __shared__ __align__(16) uint16_t Ks1[KT];
     __shared__ __align__(16) uint16_t Vs0[BK * D];
     __shared__ __align__(16) uint16_t Vs1[BK * D];
     __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
+    __shared__ float ksc[FP8 ? kMaxKeyTiles : 1];  // FP8: the scale of every 64-key tile of the head
     auto kbuf_of = [&](auto I) -> uint16_t* {
         if constexpr (decltype(I)::value == 0) return Ks0;
         else return Ks1;
@@ -467,7 +526,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int Nk = int(a.Nk);  // keys per sequence
     const uint32_t head_bytes = uint32_t(N) * D * 2u;
     const uint32_t kv_bytes = uint32_t(Nk) * D * 2u;
-    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
+    const int4v rK = FP8 ? head_desc(a.k8 + (int64_t(b) * a.Hkv + hk) * Nk * D, uint32_t(Nk) * D)
+                         : head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
     const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
 
     const int tid = threadIdx.x;
@@ -482,8 +542,16 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     int qsrc = qrow;  // source row of this lane's query; past the end it reads zeros
     if constexpr (GATHER) qsrc = row_valid ? a.perm[qrow] : N;
 
-    bf16x8_t qf[KS];
-    {
+    bf16x8_t qf[FP8 ? 1 : KS];
+    i32x8 q8f[2];
+    float qscale = 1.f;  // FP8: dequantization scale of this query block
+    if constexpr (FP8) {
+        load_q8(a.q8 + int64_t(bh) * N * D, uint32_t(N) * D, qsrc, half, q8f);
+        qscale = a.q_scale[int64_t(bh) * a.n_qb + qb];
+        const float* ks_src = a.k_scale + (int64_t(b) * a.Hkv + hk) * a.n_kt;
+        // one entry past the last tile: a 128-key block's second tile may lie wholly past the end
+        for (int x = tid; x <= a.n_kt; x += 256) ksc[x] = x < a.n_kt ? ks_src[x] : 1.f;
+    } else {
         const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -531,28 +599,36 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             for (int x = 0; x < 2; ++x) rw.src[x] = prow[t % kRing][tl.r0 + 8 * x];
         }
     };
-    // byte offsets of the two source rows; an invalid tile or a row past the
-    // end gets an offset beyond the buffer (reads zeros)
-    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2]) {
+    // byte offsets of the two source rows (rows of rs bytes); an invalid tile
+    // or a row past the end gets an offset beyond the buffer (reads zeros)
+    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2], uint32_t rs) {
         if constexpr (GATHER) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * rs : 0x80000000u;
             }
         } else {
-            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
+            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * rs;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
+            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t(tl.r0 + 8 * x) * rs;
         }
     };
     auto issue_kv = [&](const Rows& rw, auto KN) {
         uint32_t rb[2];
-        row_bytes(rw, rb);
-        const uint32_t kl = lds_addr(kbuf_of(KN)) + uint32_t(wave * DI * 1024);
+        row_bytes(rw, rb, uint32_t(D * 2));
         const uint32_t vl = lds_addr(vbuf_of(KN)) + uint32_t(wave * DI * 1024);
+        if constexpr (FP8) {  // 2 lines of 8 code rows per wave: rows r0 and r0 + 8
+            uint32_t rk[2];
+            row_bytes(rw, rk, uint32_t(D));
+            const uint32_t kl = lds_addr(kbuf_of(KN)) + uint32_t(wave * 2 * 1024);
 #pragma unroll
-        for (int c = 0; c < DI; ++c) dma16_at(rK, kl + uint32_t(c * 1024), tl.k_off(rb, c));
+            for (int c = 0; c < 2; ++c) dma16_at(rK, kl + uint32_t(c * 1024), rk[c] + tl.kch[c][0]);
+        } else {
+            const uint32_t kl = lds_addr(kbuf_of(KN)) + uint32_t(wave * DI * 1024);
+#pragma unroll
+            for (int c = 0; c < DI; ++c) dma16_at(rK, kl + uint32_t(c * 1024), tl.k_off(rb, c));
+        }
 #pragma unroll
         for (int c = 0; c < DI; ++c) dma16_at(rV, vl + uint32_t(c * 1024), tl.v_off(rb, c));
     };
@@ -561,6 +637,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
         k_off[k4] = ((l32 >> 3) * SEG * 1024 + (l32 & 7) * 128 + (((2 * k4 + half) ^ ((l32 >> 1) & 7)) * 16)) / 2;
+    int k8o[4];  // FP8: byte offsets of the K operand chunks
+    if constexpr (FP8) k8_offsets(l32, half, k8o);
     {
         const int g = (lane >> 4) & 1, j = (lane & 15) >> 2, m = lane & 3;
 #pragma unroll
@@ -573,7 +651,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
-    float m_run = -INFINITY;  // running max in raw score units (q.k)
+    float m_run = -INFINITY;  // running max in score units (q.k; FP8: of the dequantized operands)
     float l_part = 0.f;
     const float c2 = a.scale * kLog2e;
     int n_exec = 0;
@@ -598,14 +676,22 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             floatx16 s0, s1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+            // FP8: scores in code units; f turns them into q.k of the dequantized operands
+            float f = 1.f;
+            if constexpr (FP8) {
+                f = qscale * ksc[kb0 >> 6];
+                qk_fp8(reinterpret_cast<const uint8_t*>(K), k8o, q8f, s0, s1);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
-                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
-                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
+                    const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
+                    const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+                }
             }
+            const float c2t = c2 * f;
             if ((kb0 + BK > Nk) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -625,7 +711,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             float lo, hi;
             swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
-            const float m_new = max2f(m_run, max2f(lo, hi));
+            const float m_new = max2f(m_run, max2f(lo, hi) * f);
             if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
                 const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);  // 0 when m_run = -inf
                 l_part *= alpha;
@@ -638,8 +724,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
-                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
+                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
+                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
             }
             float ps[8];
 #pragma unroll
@@ -693,7 +779,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     if (nt > 1) tile_rows(1, k1, nr);
     dma_wait<0>();
     __syncthreads();
-    q_ready(qf);
+    if constexpr (FP8) q_ready(q8f);
+    else q_ready(qf);
     for (int t = 0; t < nt; t += 2) {
         step(t, I0{}, I1{});
         if (t + 1 < nt) step(t + 1, I1{}, I0{});
@@ -739,7 +826,7 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 // buffers; V needs one buffer.  The skip test of a 32-row group is one
 // ballot: skip when no valid row's block maximum comes within lambda of its
 // new running maximum.
-template <int D, bool GATHER>
+template <int D, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                  uint8_t* __restrict__ pv_skip) {
@@ -749,12 +836,16 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     constexpr int KS = D / 16;               // MFMA k-steps over the head dim
     constexpr int SEG = D / 64;              // 128-byte segments per row
     constexpr int DI = 2 * SEG;              // DMA instructions per wave per tile and tensor
-    __shared__ __align__(16) uint16_t Ks[3][BK * D];
+    static_assert(!FP8 || D == 128, "the FP8 QK path has head dim 128");
+    constexpr int DK = FP8 ? 2 : DI;         // ... for K (FP8: 8 KB tiles)
+    constexpr int KT = FP8 ? BK * D / 2 : BK * D;  // uint16 slots of one K tile
+    __shared__ __align__(16) uint16_t Ks[3][KT];
     __shared__ __align__(16) uint16_t Vs[BK * D];
     __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
     __shared__ uint32_t need[3];  // need[t % 3] bit w: wave w keeps the PV product of tile t
     // the row's column indices, kColChunk tiles per chunk, two chunks in turn
     __shared__ __align__(16) int32_t colc[2][kColChunk];
+    __shared__ float ksc[FP8 ? kMaxKeyTiles : 1];  // FP8: the scale of every 64-key tile of the head
 
     const int G = a.B * a.Hq * a.n_qb;
     const int per = (G + 7) >> 3;
@@ -769,7 +860,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int Nk = int(a.Nk);  // keys per sequence
     const uint32_t head_bytes = uint32_t(N) * D * 2u;
     const uint32_t kv_bytes = uint32_t(Nk) * D * 2u;
-    const int4v rK = head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
+    const int4v rK = FP8 ? head_desc(a.k8 + (int64_t(b) * a.Hkv + hk) * Nk * D, uint32_t(Nk) * D)
+                         : head_desc(a.k + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
     const int4v rV = head_desc(a.v + (int64_t(b) * a.Hkv + hk) * Nk * D, kv_bytes);
 
     const int tid = threadIdx.x;
@@ -784,8 +876,16 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     int qsrc = qrow;  // source row of this lane's query; past the end it reads zeros
     if constexpr (GATHER) qsrc = row_valid ? a.perm[qrow] : N;
 
-    bf16x8_t qf[KS];
-    {
+    bf16x8_t qf[FP8 ? 1 : KS];
+    i32x8 q8f[2];
+    float qscale = 1.f;  // FP8: dequantization scale of this query block
+    if constexpr (FP8) {
+        load_q8(a.q8 + int64_t(bh) * N * D, uint32_t(N) * D, qsrc, half, q8f);
+        qscale = a.q_scale[int64_t(bh) * a.n_qb + qb];
+        const float* ks_src = a.k_scale + (int64_t(b) * a.Hkv + hk) * a.n_kt;
+        // one entry past the last tile: a 128-key block's second tile may lie wholly past the end
+        for (int x = tid; x <= a.n_kt; x += 256) ksc[x] = x < a.n_kt ? ks_src[x] : 1.f;
+    } else {
         const __amdgpu_buffer_rsrc_t rQ = head_rsrc(a.q + int64_t(bh) * N * D, head_bytes);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -812,7 +912,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const TileLane<D> tl(wave, lane);
     const int4v rP = head_desc(a.perm, uint32_t(N) * 4u);
     const uint32_t pr_lds = lds_addr(&prow[0][0]);
-    const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DI * 1024);
+    const uint32_t ks_lds = lds_addr(&Ks[0][0]) + uint32_t(wave * DK * 1024);
     const uint32_t vs_lds = lds_addr(&Vs[0]) + uint32_t(wave * DI * 1024);
     // wave 0 fetches the source rows of tile t (first key key0) into ring slot t % kRing;
     // a tile past the row's end (key -1) reads zeros
@@ -837,31 +937,38 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             for (int x = 0; x < 2; ++x) rw.src[x] = prow[t % kRing][tl.r0 + 8 * x];
         }
     };
-    // byte offsets of the two source rows; an invalid tile or a row past the
-    // end gets an offset beyond the buffer (reads zeros)
-    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2]) {
+    // byte offsets of the two source rows (rows of rs bytes); an invalid tile
+    // or a row past the end gets an offset beyond the buffer (reads zeros)
+    auto row_bytes = [&](const Rows& rw, uint32_t (&rb)[2], uint32_t rs) {
         if constexpr (GATHER) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = tl.r0 + 8 * x;
-                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * uint32_t(D * 2) : 0x80000000u;
+                rb[x] = (rw.key0 >= 0 && rw.key0 + r < Nk) ? uint32_t(rw.src[x]) * rs : 0x80000000u;
             }
         } else {
-            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * uint32_t(D * 2);
+            const uint32_t base = rw.key0 < 0 ? 0x80000000u : uint32_t(rw.key0) * rs;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t((tl.r0 + 8 * x) * D * 2);
+            for (int x = 0; x < 2; ++x) rb[x] = base + uint32_t(tl.r0 + 8 * x) * rs;
         }
     };
     auto issue_k = [&](const Rows& rw, int buf) {  // this wave's share of a K tile
         uint32_t rb[2];
-        row_bytes(rw, rb);
+        if constexpr (FP8) {  // 2 lines of 8 code rows per wave: rows r0 and r0 + 8
+            row_bytes(rw, rb, uint32_t(D));
 #pragma unroll
-        for (int c = 0; c < DI; ++c)
-            dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), tl.k_off(rb, c));
+            for (int c = 0; c < 2; ++c)
+                dma16_at(rK, ks_lds + uint32_t(buf * BK * D + c * 1024), rb[c] + tl.kch[c][0]);
+        } else {
+            row_bytes(rw, rb, uint32_t(D * 2));
+#pragma unroll
+            for (int c = 0; c < DI; ++c)
+                dma16_at(rK, ks_lds + uint32_t(buf * BK * D * 2 + c * 1024), tl.k_off(rb, c));
+        }
     };
     auto issue_v = [&](const Rows& rw) {  // this wave's share of a V tile
         uint32_t rb[2];
-        row_bytes(rw, rb);
+        row_bytes(rw, rb, uint32_t(D * 2));
 #pragma unroll
         for (int c = 0; c < DI; ++c) dma16_at(rV, vs_lds + uint32_t(c * 1024), tl.v_off(rb, c));
     };
@@ -870,6 +977,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
         k_off[k4] = ((l32 >> 3) * SEG * 1024 + (l32 & 7) * 128 + (((2 * k4 + half) ^ ((l32 >> 1) & 7)) * 16)) / 2;
+    int k8o[4];  // FP8: byte offsets of the K operand chunks
+    if constexpr (FP8) k8_offsets(l32, half, k8o);
     {
         const int g = (lane >> 4) & 1, j = (lane & 15) >> 2, m = lane & 3;
 #pragma unroll
@@ -882,7 +991,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
-    float m_run = -INFINITY;  // running max in raw score units (q.k)
+    float m_run = -INFINITY;  // running max in score units (q.k; FP8: of the dequantized operands)
     float l_part = 0.f;
     const float c2 = a.scale * kLog2e;
     const float lam_raw = a.lambda / a.scale;
@@ -953,7 +1062,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     if (tid < 3) need[tid] = 0u;
     dma_wait<0>();
     __syncthreads();
-    q_ready(qf);
+    if constexpr (FP8) q_ready(q8f);
+    else q_ready(qf);
     int kbuf = 0;  // t % 3, also the need slot of tile t
     uint32_t need_prev = 0u;  // the need flags of tile t-1, read after the last barrier
     uint64_t skipm = 0ull;    // bit i: PV of tile t - t % 64 + i skipped (this wave's group)
@@ -996,18 +1106,26 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             const uint16_t* K = Ks[kbuf];
 #pragma unroll
             for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+            // FP8: scores in code units; f turns them into q.k of the dequantized operands
+            float f = 1.f;
+            if constexpr (FP8) f = qscale * ksc[kb0 >> 6];
             // the score products issue ahead of the other wave of this SIMD, whose
             // softmax then fills the VALU while the matrix core runs
             __builtin_amdgcn_s_setprio(1);
+            if constexpr (FP8) {
+                qk_fp8(reinterpret_cast<const uint8_t*>(K), k8o, q8f, s0, s1);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
-                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
-                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
+                    const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
+                    const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+                }
             }
             __builtin_amdgcn_s_setprio(0);
+            const float c2t = c2 * f;
             if ((kb0 + BK > Nk) || (a.causal && kb0 + BK - 1 > wrow0)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -1027,7 +1145,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             float lo, hi;
             swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
-            const float smax = max2f(lo, hi);
+            const float smax = max2f(lo, hi) * f;
             const float m_new = max2f(m_run, smax);
             // NaN (no key yet) and -inf gaps never reach lambda
             const bool skip = __builtin_amdgcn_ballot_w64(row_valid && smax - m_new >= lam_raw) == 0ull;
@@ -1036,8 +1154,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
-                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
+                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
+                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
             }
             float ps[8];
 #pragma unroll
@@ -1053,7 +1171,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         }
         // PV of tile t-1 once every wave's part of its V tile has landed
         if (vprev) {
-            dma_wait<DI>();
+            dma_wait<DK>();  // only the K DMAs issued after it may still be in flight
             tile_barrier();
             if (pend) apply_pending();
         }
@@ -1077,7 +1195,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         }
         // K of tile t+1 and the source rows of tile t+4 have landed (K of t+2
         // may be in flight); V reads and the need flags are complete
-        dma_wait<DI>();
+        dma_wait<DK>();
         lds_wait();
         tile_barrier();
         // every wave's need flag of tile t is in place: read it now, use it at the
@@ -1263,7 +1381,24 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
     const bool lam_on = a.lambda > -INFINITY;
     const dim3 grid{unsigned(rows), 1, 1};
     const dim3 block{256, 1, 1};
-    if (a.bq == 16 && a.bk == 16) {
+    if (a.q8) {
+        // FP8 QK path: head dim 128, 128-row query blocks, 64-key tiles (128-key
+        // blocks without PV skip); the caller has checked the shape
+        if (a.D != 128 || a.bq != 128 || (a.bk == 128 && lam_on)) return hipErrorInvalidValue;
+        if (a.n_kt != (a.Nk + 63) / 64 || a.n_kt >= kMaxKeyTiles) return hipErrorInvalidValue;
+        const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
+        const bool G = a.perm != nullptr;
+        if (a.bk == 64 && lam_on) {
+            if (G) hipLaunchKernelGGL((k_flash_lam<128, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+            else hipLaunchKernelGGL((k_flash_lam<128, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+        } else if (a.bk == 64) {
+            if (G) hipLaunchKernelGGL((k_flash_dma<128, 1, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+            else hipLaunchKernelGGL((k_flash_dma<128, 1, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+        } else {
+            if (G) hipLaunchKernelGGL((k_flash_dma<128, 2, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+            else hipLaunchKernelGGL((k_flash_dma<128, 2, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+        }
+    } else if (a.bq == 16 && a.bk == 16) {
         if (a.D == 128) hipLaunchKernelGGL(k_flash_small<128>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(k_flash_small<64>, grid, block, 0, stream, a);
     } else if (a.bk == 128 && lam_on) {
@@ -1275,14 +1410,14 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
         auto go = [&](auto gather) {
             constexpr bool G = decltype(gather)::value;
             if (a.bk == 64 && lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_lam<128, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_lam<64, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_lam<128, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_lam<64, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             } else if (a.bk == 64) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 1, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             } else {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 2, G>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
+                else hipLaunchKernelGGL((k_flash_dma<64, 2, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
             }
         };
         if (a.perm) go(std::true_type{});

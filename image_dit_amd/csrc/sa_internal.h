@@ -68,10 +68,30 @@ hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t*
                       int n_qb, int n_kb, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
                       int32_t* dev_status, hipStream_t stream);
 
+// Largest block (rows) of the FP8 quantizer.
+constexpr int kQuantMaxBlock = 128;
+// Rows per K quantization block of the FP8 attention path (the 64-key tile).
+constexpr int kKeyQuantRows = 64;
+// Most 64-key tiles per sequence on the FP8 attention path (their scales sit in LDS).
+constexpr int kMaxKeyTiles = 4096;
+
+// x: bf16 [BH, N, D]; perm: token permutation or null; codes: E4M3 [BH, N, D];
+// scales: fp32 [BH, ceil(N / block)].  D is 64 or 128, block 1..kQuantMaxBlock.
+hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* perm, int64_t BH, int64_t N, int D, int block,
+                            uint8_t* codes, float* scales, hipStream_t stream);
+
 struct FlashArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
+    // FP8 QK path (q8 non-null): E4M3 codes of Q and K in place of q and k, with
+    // one scale per query block (q_scale [B,Hq,n_qb]) and per 64-key tile
+    // (k_scale [B,Hkv,n_kt])
+    const uint8_t* q8;
+    const uint8_t* k8;
+    const float* q_scale;
+    const float* k_scale;
+    int n_kt;
     float* o;
     const int32_t* row_ptr;
     const int32_t* col_idx;

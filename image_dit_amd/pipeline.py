@@ -100,9 +100,11 @@ class SparseAttentionPath:
     """Owns the device buffers of one workload shape and runs the four entry points."""
 
     def __init__(self, cfg: PathConfig, device="cuda", col_cap: Optional[int] = None, want_skip=True,
-                 materialize=True, forced: Optional[np.ndarray] = None):
+                 materialize=True, forced: Optional[np.ndarray] = None, qk_fp8=False):
         """forced: optional host block pattern [n_qb, n_kb] (nonzero = key block always kept by
-        that query block, in every head), e.g. from ``sa_plan_tile_window``."""
+        that query block, in every head), e.g. from ``sa_plan_tile_window``.
+        qk_fp8: take the QK products on per-block E4M3 codes (sa_quantize_fp8 +
+        sa_sparse_attn_fwd_qk8) instead of bf16."""
         import torch
 
         self.cfg = cfg
@@ -140,6 +142,13 @@ class SparseAttentionPath:
         self.counters = torch.zeros(3, dtype=torch.int64, device=device)
         self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device) if materialize else None
         self.o = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
+        self.qk_fp8 = qk_fp8
+        if qk_fp8:
+            u8 = torch.uint8
+            self.q8 = torch.empty((B, Hq, N, D), dtype=u8, device=device)
+            self.k8 = torch.empty((B, Hkv, Nk, D), dtype=u8, device=device)
+            self.q_scale = torch.empty(B * Hq * cfg.n_qb, dtype=torch.float32, device=device)
+            self.k_scale = torch.empty(B * Hkv * -(-Nk // L.SA_FP8_KEY_ROWS), dtype=torch.float32, device=device)
         self.forced = None
         if forced is not None:
             forced = np.asarray(forced)
@@ -164,9 +173,24 @@ class SparseAttentionPath:
         L.sa_predict_mask(self.qp, self.kp, self.mp, self.ws, self.row_ptr, self._cols(), self.status[0:1],
                           mask_out, sim_q, sim_k, stream)
 
+    def quantize(self, q, k, perm=None, perm_k=None, stream=None):
+        """E4M3 codes and block scales of q (blocks of block_q rows) and k (64-row blocks)."""
+        L.sa_quantize_fp8(q, perm, self.cfg.block_q, self.q8, self.q_scale, stream)
+        L.sa_quantize_fp8(k, perm_k, L.SA_FP8_KEY_ROWS, self.k8, self.k_scale, stream)
+
     def attend(self, stream=None):
+        if self.qk_fp8:
+            self.quantize(self.qp, self.kp, stream=stream)
+            self.attend_qk8(stream)
+            return
         L.sa_sparse_attn_fwd(self.qp, self.kp, self.vp, self.o_perm, self.ap, self.row_ptr, self.col_idx,
                              self.status[1:2], self.pv_skip, self.counters, stream)
+
+    def attend_qk8(self, stream=None):
+        """The attention of attend on the codes of the last quantize call (FP8 QK path)."""
+        L.sa_sparse_attn_fwd_qk8(self.q8, self.q_scale, self.k8, self.k_scale, self.vp, None, self.o_perm,
+                                 self.ap, self.row_ptr, self.col_idx, self.status[1:2], self.pv_skip,
+                                 self.counters, stream)
 
     def unpermute(self, stream=None):
         L.sa_unpermute(self.o_perm, self.o, self.perm, stream)
@@ -188,8 +212,17 @@ class SparseAttentionPath:
                                  self.status[0:1], mask_out, sim_q, sim_k, stream)
 
     def attend_gather(self, q, k, v, stream=None):
+        if self.qk_fp8:
+            self.quantize(q, k, self.perm, self.perm, stream)
+            self.attend_qk8_gather(v, stream)
+            return
         L.sa_sparse_attn_fwd_gather(q, k, v, self.perm, self.o, self.ap, self.row_ptr, self.col_idx,
                                     self.status[1:2], self.pv_skip, self.counters, stream)
+
+    def attend_qk8_gather(self, v, stream=None):
+        """The attention of attend_gather on the codes of the last quantize call (FP8 QK path)."""
+        L.sa_sparse_attn_fwd_qk8(self.q8, self.q_scale, self.k8, self.k_scale, v, self.perm, self.o, self.ap,
+                                 self.row_ptr, self.col_idx, self.status[1:2], self.pv_skip, self.counters, stream)
 
     def run_fused(self, q, k, v, stream=None):
         """q, k, v: bf16 in the original token order; returns O (fp32) in the original order."""

@@ -286,6 +286,49 @@ int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const int32_t* perm
                        int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, uint8_t* mask_out,
                        float* sim_q, float* sim_k, int32_t* dev_status, void* stream);
 
+/* Rows per K quantization block of sa_sparse_attn_fwd_qk8 (the 64-key tile). */
+#define SA_FP8_KEY_ROWS 64
+
+/* Per-block 8-bit quantization of a QK operand (SpargeAttn notes, section
+ * 2.4: the sparse kernel's QK path takes Q and K quantized block by block,
+ * each block with one dequantization scale).  The format is OCP FP8 E4M3
+ * (bias 7, 3 mantissa bits, largest finite 448, subnormals, no infinities).
+ * x: device bf16 [B,H,N,D] in the ORIGINAL token order; perm_dev: device
+ * int32 [N] as for the gather calls, or NULL (identity).  Block j of each
+ * (b, h) is the rows perm[j*block .. j*block+block-1] (the last block may be
+ * short).  With amax = max |x| over the block (float32):
+ *   scales[b,h,j] = amax / 448          (1 when amax = 0)
+ *   codes[b,h,r,:] = E4M3 code nearest to clamp(x[b,h,r,:] * (448 / amax),
+ *                    -448, 448), ties to even, sign kept, for every row r of
+ *                    block j, written at the row's own (original) position
+ * amax, both divisions and the product are IEEE float32 operations.
+ * codes: device uint8 [B,H,N,D] (8-byte aligned), scales: device fp32
+ * [B,H,ceil(N/block)].  D is 64 or 128 (else SA_ERR_UNSUPPORTED); block is
+ * 1..128.  Q takes block = block_q, K takes block = SA_FP8_KEY_ROWS.  An
+ * entry of perm_dev outside 0..N-1 makes its row take no part (nothing is
+ * read or written for it). */
+int sa_quantize_fp8(const uint16_t* x, const int32_t* perm_dev, int32_t B, int32_t H, int64_t N,
+                    int32_t D, int32_t block, uint8_t* codes, float* scales, void* stream);
+
+/* sa_sparse_attn_fwd (perm_dev NULL) or sa_sparse_attn_fwd_gather (perm_dev
+ * non-NULL) with the QK products taken on FP8 operands (SpargeAttn notes,
+ * section 2.4; the SageAttention idea on the gfx950 FP8 matrix cores): the
+ * score of query row i and key j is
+ *   (q8[i] . k8[j]) * q_scale[block of i] * k_scale[tile of j] * scale,
+ * the dot product of the E4M3 values taken exactly and summed in fp32; the
+ * softmax, the PV-skip rule and the P V products (v in bf16) are those of
+ * sa_sparse_attn_fwd.  q8: device uint8 [B,Hq,N,D] with q_scale device fp32
+ * [B,Hq,ceil(N/block_q)]; k8: device uint8 [B,Hkv,N_k,D] with k_scale device
+ * fp32 [B,Hkv,ceil(N_k/SA_FP8_KEY_ROWS)], both as written by sa_quantize_fp8
+ * (with the same perm_dev).  Needs D = 128, block_q = 128, and block_k = 64,
+ * or block_k = 128 with lambda off; ceil(N_k/64) below 4096 (else
+ * SA_ERR_UNSUPPORTED).  q8 and k8 16-byte aligned.  Other arguments, errors
+ * and outputs as in sa_sparse_attn_fwd / sa_sparse_attn_fwd_gather. */
+int sa_sparse_attn_fwd_qk8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                           const float* k_scale, const uint16_t* v, const int32_t* perm_dev, float* o,
+                           const sa_attn_params* p, const int32_t* row_ptr, const int32_t* col_idx,
+                           uint8_t* pv_skip, int64_t* counters, int32_t* dev_status, void* stream);
+
 /* Bytes of the fixed device workspace of sa_predict_mask_gather_noalloc
  * (64 MiB, one copy per GPU for the life of the process). */
 #define SA_NOALLOC_SCRATCH_BYTES (64ll << 20)

@@ -26,7 +26,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(sa.LIB_PATH), reason="library
 def _declared_functions():
     text = open(HEADER, encoding="utf8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -395,3 +395,57 @@ def test_noalloc_prediction_refuses_workspaces_over_its_array():
     rc = L.sa_predict_mask_gather_noalloc(fake, fake, None, ctypes.byref(big), fake, fake, 0, None, None, None,
                                           fake, None)
     assert rc == sa.SA_ERR_INVALID_ARGUMENT
+
+
+# ------------------------------------------------------------------ FP8 QK entry points
+
+def _quant_code(x=FAKE, perm=None, B=1, H=2, N=1000, D=128, block=64, codes=FAKE, scales=FAKE):
+    return sa.lib().sa_quantize_fp8(x, perm, B, H, N, D, block, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(block=0), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(block=129), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(D=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(x=None), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(codes=None), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(scales=None), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(x=ctypes.c_void_p((1 << 20) + 8)), sa.SA_ERR_INVALID_ARGUMENT),
+    (dict(codes=ctypes.c_void_p((1 << 20) + 4)), sa.SA_ERR_INVALID_ARGUMENT),
+])
+def test_quantize_fp8_rejects_bad_arguments(kw, code):
+    assert _quant_code(**kw) == code
+
+
+def _qk8_code(p, perm=None, **ptrs):
+    args = dict(q8=FAKE, qs=FAKE, k8=FAKE, ks=FAKE, v=FAKE, o=FAKE, row_ptr=FAKE, col_idx=FAKE, status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_sparse_attn_fwd_qk8(args["q8"], args["qs"], args["k8"], args["ks"], args["v"], perm,
+                                           args["o"], ctypes.byref(p), args["row_ptr"], args["col_idx"], None, None,
+                                           args["status"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), sa.SA_ERR_UNSUPPORTED),                          # FP8 QK path: head dim 128 only
+    (dict(block_q=16, block_k=16, D=128), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_k=128, lam=-8.0), sa.SA_ERR_UNSUPPORTED),         # 128-key blocks: lambda off only
+    (dict(N=4096 * 64), sa.SA_ERR_UNSUPPORTED),                   # key-tile scales must fit the table
+    (dict(lam=0.5), sa.SA_ERR_INVALID_ARGUMENT),
+])
+def test_qk8_rejects_unsupported_shapes(kw, code):
+    base = dict(B=1, Hq=4, Hkv=2, N=1000, D=128, block_q=128, block_k=64)
+    base.update(kw)
+    assert _qk8_code(sa.make_attn_params(**base)) == code
+
+
+def test_qk8_rejects_bad_buffers():
+    p = sa.make_attn_params(1, 4, 2, 1000, 128, 128, 64, lam=-8.0)
+    assert _qk8_code(p, q8=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, k8=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, qs=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, ks=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, v=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, q8=ctypes.c_void_p((1 << 20) + 8)) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _qk8_code(p, ks=ctypes.c_void_p((1 << 20) + 2)) == sa.SA_ERR_INVALID_ARGUMENT
