@@ -67,7 +67,9 @@ int predict_shape(const sa_mask_params* p, PredictShape* s) {
     s->off[2] = o; o = align_up(o + qblk * 4);
     s->off[3] = o; o = align_up(o + kblk * 4);
     s->off[4] = o; o = align_up(o + qblk * s->n_kb);
-    s->off[5] = o; o = align_up(o + (qblk + topcdf_groups(int64_t(p->B) * p->Hq, s->n_qb)) * 4);
+    // row counts, group totals, super-group totals
+    const int64_t groups = topcdf_groups(int64_t(p->B) * p->Hq, s->n_qb);
+    s->off[5] = o; o = align_up(o + (qblk + groups + (groups + kSuperGroups - 1) / kSuperGroups) * 4);
     s->bytes = size_t(o);
     return SA_OK;
 }
@@ -173,12 +175,17 @@ int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm,
     uint8_t* mask = reinterpret_cast<uint8_t*>(base + s.off[4]);
     int32_t* counts = reinterpret_cast<int32_t*>(base + s.off[5]);
 
-    hipError_t e = launch_block_stats(q, k, perm, s, qbar, kbar, simq, simk, dev_status, hs);
+    const int64_t n_groups = topcdf_groups(int64_t(s.B) * s.Hq, s.n_qb);
+    const int64_t n_super = (n_groups + kSuperGroups - 1) / kSuperGroups;
+    int32_t* super_tot = counts + s.rows + n_groups;
+    hipError_t e = launch_block_stats(q, k, perm, s, qbar, kbar, simq, simk, dev_status, super_tot, int(n_super),
+                                      hs);
     if (e != hipSuccess) return SA_ERR_HIP;
 
     TopCdfArgs a;
     a.qbar = qbar; a.kbar = kbar; a.simq = simq; a.simk = simk;
     a.mask = mask; a.counts = counts; a.group_tot = counts + s.rows; a.forced = forced;
+    a.super_tot = super_tot;
     a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.N = s.N;
     a.bq = s.bq; a.bk = s.bk; a.n_qb = int(s.n_qb); a.n_kb = int(s.n_kb); a.Nk = s.Nk;
     a.causal = p->causal; a.window = p->window;

@@ -11,8 +11,13 @@
 //                  guard/sink/window forcing, the softmax over the candidates,
 //                  an exact radix selection for TopCdf and the keep floor, the
 //                  dense mask row, its kept count and the group's total.
-//   k_csr          per group: row offsets from the group totals, then the
-//                  ascending column lists from the mask rows (ballot compaction).
+//                  Each group's total is also added (a relaxed atomic) to
+//                  the total of its super-group of kSuperGroups groups.
+//   k_csr          per group: the first row offset from the super-group totals
+//                  before it and the group totals before it in its own
+//                  super-group (at most G/256 + 255 reads), the group's row
+//                  offsets, then the ascending column lists from the mask rows
+//                  (ballot compaction).
 #include <cfloat>
 #include <type_traits>
 
@@ -52,11 +57,6 @@ __device__ inline float wave_sum(float v) { return wave_reduce(v, [](float x, fl
 __device__ inline float wave_max(float v) { return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); }); }
 __device__ inline int wave_sum_i(int v) { return wave_reduce(v, [](int x, int y) { return x + y; }); }
 __device__ inline uint32_t wave_sum_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; }); }
-__device__ inline long long wave_sum_ll(long long v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
 
 // DPP lane move; lanes without a source (or in a disabled row) read 0.
 template <int CTRL, int ROW_MASK = 0xf>
@@ -116,11 +116,14 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
                                                      int bq, int bk, int64_t q_blocks, int64_t all_blocks,
                                                      int n_qb, int n_kb, float* __restrict__ qbar,
                                                      float* __restrict__ kbar, float* __restrict__ simq,
-                                                     float* __restrict__ simk, int32_t* dev_status) {
+                                                     float* __restrict__ simk, int32_t* dev_status,
+                                                     int32_t* super_tot, int n_super) {
     constexpr int CH = D / 8;
     constexpr int RPW = 64 / CH;   // rows per wave step
     constexpr int U = 8;           // steps in flight
     if (blockIdx.x == 0 && threadIdx.x == 0) *dev_status = SA_OK;
+    // the super-group totals the TopCdf launch adds to (the grid has more workgroups)
+    if (threadIdx.x == 0 && int64_t(blockIdx.x) < n_super) super_tot[blockIdx.x] = 0;
     const int lane = threadIdx.x & 63;
     const int64_t blk = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (blk >= all_blocks) return;
@@ -548,6 +551,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
 // blocks 2w and 2w+1.  Dynamic LDS: scores[16][ls] f32 | per wavefront:
 // histogram[256] u32 | column forcing bits[ceil(n_kb/32)] u32.
 constexpr int kTopcdfWaves = 8;
+
 template <int D>
 __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls, int gr) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -633,18 +637,23 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
 #pragma unroll
         for (int w = 0; w < kTopcdfWaves; ++w) sum += wave_tot[w];
         a.group_tot[blockIdx.x] = sum;
+        // read only by the next launch: no ordering needed here
+        __hip_atomic_fetch_add(&a.super_tot[blockIdx.x / kSuperGroups], sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---------------------------------------------------------------- CSR
 // One workgroup per group of gr query blocks (the TopCdf grouping).  Its
-// first row offset is the sum of the totals of all earlier groups; the
-// group's own rows are scanned by one wavefront; then each wavefront
-// compacts four mask rows into ascending column lists.
+// first row offset is the sum of the super-group totals before its own
+// super-group and of the group totals before it inside that one; the group's
+// own rows are scanned by one wavefront; then each wavefront compacts four
+// mask rows into ascending column lists.
 constexpr int kMaxWordsPerLane = SA_MAX_KEY_BLOCKS / 256;
 
 __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, const int32_t* __restrict__ counts,
-                                             const int32_t* __restrict__ group_tot, int n_groups,
+                                             const int32_t* __restrict__ group_tot,
+                                             const int32_t* __restrict__ super_tot, int n_groups,
                                              int groups_per_head, int gr, int n_qb, int n_kb, int64_t rows,
                                              int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
                                              int64_t col_cap, int32_t* dev_status) {
@@ -655,10 +664,15 @@ __global__ __launch_bounds__(256) void k_csr(const uint8_t* __restrict__ mask, c
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
+    // rows before this group: whole super-groups, then the groups before it in its own
+    const int sg = g / kSuperGroups;
     long long s = 0;
-    for (int t = tid; t < g; t += 256) s += group_tot[t];
-    s = wave_sum_ll(s);
+    for (int t = tid; t < sg; t += 256) s += super_tot[t];
+    if (sg * kSuperGroups + tid < g) s += group_tot[sg * kSuperGroups + tid];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
     if (lane == 0) red[wave] = s;
+
     const int bh = g / groups_per_head;
     const int i0 = (g - bh * groups_per_head) * gr;
     const int nr = min(gr, n_qb - i0);
@@ -761,20 +775,20 @@ int64_t topcdf_groups(int64_t bh, int64_t n_qb) {
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk, int32_t* dev_status,
-                              hipStream_t stream) {
+                              int32_t* super_tot, int n_super, hipStream_t stream) {
     const int64_t qb = int64_t(s.B) * s.Hq * s.n_qb;
     const int64_t kb = int64_t(s.B) * s.Hkv * s.n_kb;
     const int64_t wgs = (qb + kb + 3) / 4;
-    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    if (wgs > INT32_MAX || n_super > wgs) return hipErrorInvalidValue;
     const dim3 grid{unsigned(wgs), 1, 1};
     auto go = [&](auto gather) {
         constexpr bool G = decltype(gather)::value;
         if (s.D == 128)
             hipLaunchKernelGGL((k_block_stats<128, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
-                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
+                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status, super_tot, n_super);
         else
             hipLaunchKernelGGL((k_block_stats<64, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
-                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status);
+                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status, super_tot, n_super);
     };
     if (perm) go(std::true_type{});
     else go(std::false_type{});
@@ -806,7 +820,7 @@ hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t*
     const int gr = topcdf_group_rows(bh, n_qb);
     const int gph = (n_qb + gr - 1) / gr;
     hipLaunchKernelGGL(k_csr, dim3(unsigned(n_groups)), dim3(256), 0, stream, mask, counts, group_tot,
-                       int(n_groups), gph, gr, n_qb, n_kb, bh * n_qb, row_ptr, col_idx, col_cap, dev_status);
+                       group_tot + n_groups, int(n_groups), gph, gr, n_qb, n_kb, bh * n_qb, row_ptr, col_idx, col_cap, dev_status);
     return hipGetLastError();
 }
 

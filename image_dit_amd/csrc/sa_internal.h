@@ -41,6 +41,7 @@ struct TopCdfArgs {
     uint8_t* mask;
     int32_t* counts;
     int32_t* group_tot;  // kept blocks per group of query blocks (topcdf_group_rows)
+    int32_t* super_tot;  // kept blocks per kSuperGroups consecutive groups (zeroed beforehand)
     const uint8_t* forced;  // [n_qb][n_kb] forced block pattern shared by all heads, or null
     int B, Hq, Hkv, D;
     int64_t N;
@@ -60,10 +61,12 @@ struct TopCdfArgs {
 // perm: token permutation (q and k in the original order), or null
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk,
-                              int32_t* dev_status, hipStream_t stream);
+                              int32_t* dev_status, int32_t* super_tot, int n_super, hipStream_t stream);
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream);
-// Number of TopCdf groups (16 consecutive query blocks of one head).
+// Number of TopCdf groups (8..16 consecutive query blocks of one head).
 int64_t topcdf_groups(int64_t bh, int64_t n_qb);
+// Groups per super-group of the CSR offsets.
+constexpr int kSuperGroups = 256;
 hipError_t launch_csr(const uint8_t* mask, const int32_t* counts, const int32_t* group_tot, int64_t bh,
                       int n_qb, int n_kb, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
                       int32_t* dev_status, hipStream_t stream);

@@ -181,8 +181,9 @@ size_t sa_predict_workspace_bytes(const sa_mask_params* p);
  * off[3] key-block similarity fp32 [B,Hkv,n_kb]; off[4] block mask uint8
  * [B,Hq,n_qb,n_kb]; off[5] kept blocks per row int32 [B*Hq*n_qb],
  * followed by the kept blocks of each group of g consecutive query blocks of
- * one head, int32 [B*Hq*ceil(n_qb/g)], g in 8..16 chosen from B*Hq and n_qb
- * (sa_predict_workspace_bytes accounts for it).
+ * one head, int32 [G], G = B*Hq*ceil(n_qb/g), g in 8..16 chosen from B*Hq
+ * and n_qb, and by the kept blocks of each run of 256 consecutive groups,
+ * int32 [ceil(G/256)] (sa_predict_workspace_bytes accounts for both).
  * Returns SA_OK or SA_ERR_INVALID_ARGUMENT. */
 int sa_predict_workspace_offsets(const sa_mask_params* p, int64_t off[6]);
 
