@@ -283,3 +283,59 @@ def test_fp8_mask_unchanged():
     ra, ca = a.csr_host()
     rb, cb = b.csr_host()
     assert np.array_equal(ra, rb) and np.array_equal(ca, cb)
+
+
+# ------------------------------------------------------------------ full size
+
+@pytest.mark.parametrize("name", ["long_video", "video"])
+def test_fp8_full_size_sampled(name):
+    """The FP8 step as `bench.py --qk fp8` runs it (gather form, full size): the codes and
+    scales of sampled blocks bit-exact, and the outputs of sampled query blocks of two heads
+    against fp64 over the dequantized operands on the GPU's CSR (PV decisions replayed)."""
+    w = CONFIGS[name]
+    log(f"[fp8 full] {name}: B={w.B} Hq={w.Hq} N={w.N} bq={w.block_q} bk={w.block_k} lam={w.lam}")
+    q, k, v = generate(w)
+    cfg = sa.config_from_workload(w)
+    path = sa.SparseAttentionPath(cfg, materialize=False, qk_fp8=True)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    path.predict_gather(qd, kd)
+    path.attend_gather(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert path.statuses() == (sa.SA_OK, sa.SA_OK)
+    del qd, kd, vd
+    perm = R.oracle_perm(w)
+    rp, ci = path.csr_host()
+    skip = path.pv_skip.cpu().numpy()
+    q8 = path.q8.cpu().numpy()
+    k8 = path.k8.cpu().numpy()
+    qs = path.q_scale.cpu().numpy().reshape(w.B, w.Hq, -1)
+    ks = path.k_scale.cpu().numpy().reshape(w.B, w.Hkv, -1)
+    rng = np.random.default_rng(7)
+    G = w.Hq // w.Hkv
+    err_max = err_sum = 0.0
+    err_n = lam_far = 0
+    for h in (0, w.Hq - 1):
+        hk = h // G
+        # the oracle's codes of this head, in the reordered order
+        qp, kp = R.permuted(q[:, h:h + 1], perm)[0, 0], R.permuted(k[:, hk:hk + 1], perm)[0, 0]
+        cq, sq = OQ.quantize_blocks(qp, w.block_q)
+        ck, sk = OQ.quantize_blocks(kp, OQ.KEY_QUANT_ROWS)
+        assert np.array_equal(q8[0, h][perm], cq) and np.array_equal(qs[0, h].view(np.uint32), sq.view(np.uint32))
+        assert np.array_equal(k8[0, hk][perm], ck) and np.array_equal(ks[0, hk].view(np.uint32), sk.view(np.uint32))
+        qh = OQ.dequantize_blocks(cq, sq, w.block_q)
+        kh = OQ.dequantize_blocks(ck, sk, OQ.KEY_QUANT_ROWS)
+        vp = R.permuted(v[:, hk:hk + 1], perm)[0, 0]
+        r0 = h * cfg.n_qb
+        blocks = sorted(set(rng.integers(0, cfg.n_qb, 6).tolist()) | {cfg.n_qb - 1})
+        ys, recs = R.attend_rows(qh, kh, vp, w, rp, ci, r0, blocks, skip, path.groups)
+        o = path.o[0, h][torch.from_numpy(perm.astype(np.int64)).cuda()].cpu().numpy()
+        for i, y in ys.items():
+            d = np.abs(o[i * w.block_q:i * w.block_q + y.shape[0]] - y)
+            err_max = max(err_max, float(d.max()))
+            err_sum += float(d.sum())
+            err_n += d.size
+            if w.lam is not None:
+                lam_far += R.lambda_disagreements(recs[i], w.lam)[0]
+    log(f"[fp8 full] {name}: out_max={err_max:.3e} out_mean={err_sum / err_n:.3e} lam_far={lam_far}")
+    assert err_max <= R.MAX_ABS and err_sum / err_n <= R.MEAN_ABS
+    assert lam_far == 0
