@@ -431,17 +431,23 @@ __device__ inline void k8_offsets(int l32, int half, int (&off)[4]) {
         for (int x = 0; x < 2; ++x)
             off[2 * ks + x] = (l32 >> 3) * 1024 + (l32 & 7) * 128 + (((4 * ks + 2 * half + x) ^ ((l32 >> 1) & 7)) * 16);
 }
-// raw scores of a 64-key FP8 tile: s0 keys 0..31, s1 keys 32..63 (code units)
-__device__ inline void qk_fp8(const uint8_t* K8, const int (&off)[4], const i32x8 (&qf)[2], floatx16& s0,
-                              floatx16& s1) {
+// this lane's K operands of a 64-key FP8 tile: kf[2 ks] for keys 0..31, kf[2 ks + 1]
+// for keys 32..63
+__device__ inline void load_k8(const uint8_t* K8, const int (&off)[4], i32x8 (&kf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const uint8_t* p = K8 + off[2 * ks];
         const uint8_t* p1 = K8 + off[2 * ks + 1];
-        const i32x8 a0 = cat8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p1));
-        const i32x8 a1 = cat8(*reinterpret_cast<const uint4*>(p + 4096), *reinterpret_cast<const uint4*>(p1 + 4096));
-        s0 = mfma_fp8(a0, qf[ks], s0);
-        s1 = mfma_fp8(a1, qf[ks], s1);
+        kf[2 * ks] = cat8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p1));
+        kf[2 * ks + 1] = cat8(*reinterpret_cast<const uint4*>(p + 4096), *reinterpret_cast<const uint4*>(p1 + 4096));
+    }
+}
+// raw scores of a 64-key FP8 tile: s0 keys 0..31, s1 keys 32..63 (code units)
+__device__ inline void qk_fp8(const i32x8 (&kf)[4], const i32x8 (&qf)[2], floatx16& s0, floatx16& s1) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        s0 = mfma_fp8(kf[2 * ks], qf[ks], s0);
+        s1 = mfma_fp8(kf[2 * ks + 1], qf[ks], s1);
     }
 }
 // vmcnt(N): at most N of this wave's vector memory operations outstanding
@@ -680,7 +686,9 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             float f = 1.f;
             if constexpr (FP8) {
                 f = qscale * ksc[kb0 >> 6];
-                qk_fp8(reinterpret_cast<const uint8_t*>(K), k8o, q8f, s0, s1);
+                i32x8 kf[4];
+                load_k8(reinterpret_cast<const uint8_t*>(K), k8o, kf);
+                qk_fp8(kf, q8f, s0, s1);
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -842,7 +850,9 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     __shared__ __align__(16) uint16_t Ks[3][KT];
     __shared__ __align__(16) uint16_t Vs[BK * D];
     __shared__ __align__(16) int32_t prow[GATHER ? kRing : 1][BK];  // source rows of tile t in slot t % kRing
-    __shared__ uint32_t need[3];  // need[t % 3] bit w: wave w keeps the PV product of tile t
+    // need[t % 3] byte w: wave w keeps the PV product of tile t (each wave stores its own
+    // byte every tile, so no slot needs clearing; the four bytes read as one word)
+    __shared__ __align__(4) uint8_t need[3][4];
     // the row's column indices, kColChunk tiles per chunk, two chunks in turn
     __shared__ __align__(16) int32_t colc[2][kColChunk];
     __shared__ float ksc[FP8 ? kMaxKeyTiles : 1];  // FP8: the scale of every 64-key tile of the head
@@ -1059,17 +1069,31 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         issue_k(kr, 1);
     }
     if (nt > 2) tile_rows(k2, 2, kr);
-    if (tid < 3) need[tid] = 0u;
     dma_wait<0>();
     __syncthreads();
     if constexpr (FP8) q_ready(q8f);
     else q_ready(qf);
+    // bf16: K operands of the next tile's first KPRE k-steps, read right after the barrier
+    // that publishes its buffer, so the first score products do not wait for them (the FP8
+    // tile's eight operand reads are issued with its products: prefetching them was slower)
+    constexpr int KPRE = KS < 4 ? KS : 4;
+    bf16x8_t kpre[FP8 ? 1 : 2 * KPRE];
+    auto prefetch_k = [&](int buf) {
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int ks = 0; ks < KPRE; ++ks) {
+                const uint16_t* Kk = Ks[buf] + k_off[ks];
+                kpre[2 * ks] = *reinterpret_cast<const bf16x8_t*>(Kk);
+                kpre[2 * ks + 1] = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
+            }
+        }
+    };
+    prefetch_k(0);
     int kbuf = 0;  // t % 3, also the need slot of tile t
     uint32_t need_prev = 0u;  // the need flags of tile t-1, read after the last barrier
     uint64_t skipm = 0ull;    // bit i: PV of tile t - t % 64 + i skipped (this wave's group)
     for (int t = 0; t < nt; ++t) {
         const int kb0 = kc;
-        const int slot_next = kbuf == 2 ? 0 : kbuf + 1;  // (t + 1) % 3 == (t - 2) % 3
         // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
         const uint32_t need_s = __builtin_amdgcn_readfirstlane(need_prev);
         const bool vprev = t > 0 && need_s != 0u;
@@ -1085,8 +1109,6 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             for (int h = 0; h < kColChunk / 256; ++h)
                 dma16_at(rC, cl + uint32_t(h * 1024), uint32_t(t + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
         }
-        // the mask of tile t-2 was read during iteration t-1: clear it for tile t+1
-        if (tid == 0) need[slot_next] = 0u;
         // prefetches past the row's end (key -1) read zeros into buffers nobody reads,
         // so they need no condition
         if (GATHER) issue_perm(t + 4, k4);
@@ -1113,13 +1135,16 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             // softmax then fills the VALU while the matrix core runs
             __builtin_amdgcn_s_setprio(1);
             if constexpr (FP8) {
-                qk_fp8(reinterpret_cast<const uint8_t*>(K), k8o, q8f, s0, s1);
+                i32x8 kf[4];
+                load_k8(reinterpret_cast<const uint8_t*>(K), k8o, kf);
+                qk_fp8(kf, q8f, s0, s1);
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const uint16_t* Kk = K + k_off[ks & 3] + (ks >> 2) * 512;
-                    const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Kk);
-                    const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
+                    const bf16x8_t k0 = ks < KPRE ? kpre[2 * ks] : *reinterpret_cast<const bf16x8_t*>(Kk);
+                    const bf16x8_t k1 =
+                        ks < KPRE ? kpre[2 * ks + 1] : *reinterpret_cast<const bf16x8_t*>(Kk + 4 * SEG * 512);
                     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
                 }
@@ -1152,10 +1177,27 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             alpha = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;  // 0 when m_run = -inf
             m_run = m_new;
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
+            if constexpr (!FP8) {
+                // every exponent argument first, in place, then the exponentials: no
+                // instruction waits on the one just before it (measured faster for bf16
+                // scores, slower for the shorter FP8 score phase)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
-                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
+                for (int i = 0; i < 16; ++i) {
+                    s0[i] = fmaf(s0[i], c2t, -mc);
+                    s1[i] = fmaf(s1[i], c2t, -mc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s0[i] = __builtin_amdgcn_exp2f(s0[i]);
+                    s1[i] = __builtin_amdgcn_exp2f(s1[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
+                    s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
+                }
             }
             float ps[8];
 #pragma unroll
@@ -1187,7 +1229,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             palpha = alpha;
         }
-        if (lane == 0 && my_need) atomicOr(&need[kbuf], 1u << wave);
+        if (lane == 0) need[kbuf][wave] = uint8_t(my_need);
         // the skip flags of 64 tiles leave in one store (lane i: tile t - t % 64 + i)
         if (pv_skip && ((t & 63) == 63 || t == nt - 1)) {
             if (lane <= (t & 63)) pv_skip[int64_t(e0 + (t & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
@@ -1200,8 +1242,9 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         tile_barrier();
         // every wave's need flag of tile t is in place: read it now, use it at the
         // top of the next iteration
-        need_prev = need[kbuf];
+        need_prev = *reinterpret_cast<const uint32_t*>(need[kbuf]);
         kbuf = kbuf == 2 ? 0 : kbuf + 1;
+        prefetch_k(kbuf);
         kc = k1;
         k1 = k2;
         k2 = k3;
