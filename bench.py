@@ -19,9 +19,10 @@ Prints ONE JSON line.  ``value`` is executed TFLOP/s of the whole step
 workload (rank 0, N=1 only).
 
 ``--qk fp8`` times the FP8 QK variant instead (Q and K quantized to per-block
-E4M3 codes inside each step, QK products on the fp8 matrix cores, P V in
-bf16); its roofline peak is the time-weighted mix of the fp8 and bf16 peaks
-over its QK and PV flops, and it has no oracle leg.
+E4M3 codes inside each step -- in the gather form by the mask prediction's
+own pass over them --, QK products on the fp8 matrix cores, P V in bf16);
+its roofline peak is the time-weighted mix of the fp8 and bf16 peaks over
+its QK and PV flops, and it has no oracle leg.
 
 Extra modes (not the benchmark line):
   --mode attn      only the sparse attention launch, repeated (for rocprofv3 counters)
@@ -299,13 +300,13 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     torch.cuda.synchronize()
 
-    # the step's stages; the gather form has no separate reorder copies; the FP8 QK
-    # path quantizes Q and K (its own stage) before the attention
+    # the step's stages; the gather form has no separate reorder copies; with FP8 QK
+    # operands the gather form's prediction writes the codes in its pass over Q and K,
+    # and the materialising form quantizes the reordered copies (its own stage)
     if gather:
         stages = [("permute", lambda: None), ("predict", lambda: path.predict_gather(qd, kd))]
         if fp8:
-            stages += [("quantize", lambda: path.quantize(qd, kd, path.perm, path.perm)),
-                       ("attn", lambda: path.attend_qk8_gather(vd))]
+            stages += [("attn", lambda: path.attend_qk8_gather(vd))]
         else:
             stages += [("attn", lambda: path.attend_gather(qd, kd, vd))]
         stages += [("unpermute", lambda: None)]
@@ -402,7 +403,9 @@ def main():
     n_qb, n_kb = cfg.n_qb, cfg.n_kb
     pred_bytes = (2 * (B * Hq * N * d + B * Hkv * N * d) + 4 * (B * Hq * n_qb + B * Hkv * n_kb) * d
                   + 4 * (B * Hq * n_qb + B * Hkv * n_kb) + 2 * B * Hq * n_qb * n_kb
-                  + 4 * (B * Hq * n_qb + 1) + 4 * nnz + (4 * N if gather else 0))
+                  + 4 * (B * Hq * n_qb + 1) + 4 * nnz + (4 * N if gather else 0)
+                  # FP8, gather form: the codes of Q and K are written in the same pass
+                  + ((B * Hq * N * d + B * Hkv * N * d) if (fp8 and gather) else 0))
     perm_bytes = (B * Hq * N * d + 2 * B * Hkv * N * d) * ((4 if w.dtype == "f32" else 2) + 2)
     unperm_bytes = 2 * 4 * B * Hq * N * d
     # quantize: Q and K read (bf16) and written (one byte per element), plus the scales
@@ -451,8 +454,8 @@ def main():
         "attn_mfma_frac": round(attn_tflops / peak, 4),
         "dense_equiv_tflops_step": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
         "dense_equiv_tflops_attn_plus_predict": round(
-            dense_flops / ((attn_ms + stage[idx["predict"]] + (stage[idx["quantize"]] if fp8 else 0.0)) * 1e-3)
-            / 1e12, 2),
+            dense_flops / ((attn_ms + stage[idx["predict"]] + (stage[idx["quantize"]] if "quantize" in idx else 0.0))
+                           * 1e-3) / 1e12, 2),
         "executed_tflop": round(exec_flops / 1e12, 4),
         "dense_tflop": round(dense_flops / 1e12, 4),
         "mask_sparsity": round(mask_sparsity, 4),
@@ -462,7 +465,8 @@ def main():
         "predict_hbm_frac": round(pred_bytes / (stage[idx["predict"]] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         **({} if gather else {"permute_gbs": round(perm_bytes / (stage[idx["permute"]] * 1e-3) / 1e9, 1),
                               "unpermute_gbs": round(unperm_bytes / (stage[idx["unpermute"]] * 1e-3) / 1e9, 1)}),
-        **({} if not fp8 else {"quantize_gbs": round(quant_bytes / (stage[idx["quantize"]] * 1e-3) / 1e9, 1)}),
+        **({} if "quantize" not in idx else
+           {"quantize_gbs": round(quant_bytes / (stage[idx["quantize"]] * 1e-3) / 1e9, 1)}),
         "roofline": {
             "bound": "mfma",
             "kernel": attn_kernel_name(cfg, gather, fp8) + " (+ k_attn_init), per "

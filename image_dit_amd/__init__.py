@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     sa_predict_mask, sa_predict_mask_ex, sa_predict_mask_gather_noalloc, SA_NOALLOC_SCRATCH_BYTES,
     sa_predict_workspace_bytes, sa_predict_workspace_offsets, sa_sparse_attn_fwd, sa_status_string,
     sa_unpermute, SA_FP8_KEY_ROWS, sa_quantize_fp8, sa_sparse_attn_fwd_qk8, sa_predict_mask_gather,
-    sa_sparse_attn_fwd_gather)
+    sa_sparse_attn_fwd_gather, sa_predict_mask_qk8)
 from .pipeline import PathConfig, SparseAttentionPath, config_from_workload  # noqa: F401

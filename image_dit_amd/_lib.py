@@ -32,7 +32,7 @@ EXPORTS = ("sa_status_string", "sa_plan_permutation", "sa_permute", "sa_unpermut
            "sa_predict_workspace_bytes", "sa_predict_workspace_offsets", "sa_predict_mask",
            "sa_sparse_attn_fwd", "sa_predict_mask_gather", "sa_sparse_attn_fwd_gather",
            "sa_plan_tile_window", "sa_predict_mask_ex", "sa_predict_mask_gather_noalloc",
-           "sa_quantize_fp8", "sa_sparse_attn_fwd_qk8")
+           "sa_quantize_fp8", "sa_sparse_attn_fwd_qk8", "sa_predict_mask_qk8")
 
 
 class SaLayout(ctypes.Structure):
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
                                          POINTER(SaAttnParams), c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p]
     L.sa_sparse_attn_fwd_qk8.restype = c_int
+    L.sa_predict_mask_qk8.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(SaMaskParams), c_void_p, c_size_t,
+                                      c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p]
+    L.sa_predict_mask_qk8.restype = c_int
     _lib = L
     return L
 
@@ -347,3 +351,20 @@ def sa_sparse_attn_fwd_qk8(q8, q_scale, k8, k_scale, v, perm, o, p: SaAttnParams
                                         _ptr(o), ctypes.byref(p), _ptr(row_ptr), _ptr(col_idx), _ptr(pv_skip),
                                         _ptr(counters), _ptr(dev_status), _stream(stream))
     _check(code, "sa_sparse_attn_fwd_qk8")
+
+
+def sa_predict_mask_qk8(q, k, perm, p: SaMaskParams, ws, row_ptr, col_idx, q8, q_scale, k8, k_scale, dev_status,
+                        stream=None):
+    """sa_predict_mask_ex (perm None: q, k already reordered) that also writes the E4M3 codes and
+    block scales sa_quantize_fp8 would write for q and k."""
+    _need(_a(q, "q", "bfloat16"), _a(k, "k", "bfloat16"), _a(perm, "perm", "int32", optional=True),
+          _a(ws, "ws", "uint8"), _a(row_ptr, "row_ptr", "int32"), _a(col_idx, "col_idx", "int32"),
+          _a(q8, "q8", "uint8"), _a(q_scale, "q_scale", "float32"), _a(k8, "k8", "uint8"),
+          _a(k_scale, "k_scale", "float32"), _a(dev_status, "dev_status", "int32"))
+    if tuple(q8.shape) != tuple(q.shape) or tuple(k8.shape) != tuple(k.shape):
+        raise ValueError("q8 and k8 must have the shapes of q and k")
+    code = lib().sa_predict_mask_qk8(_ptr(q), _ptr(k), _ptr(perm), ctypes.byref(p), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                     _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(dev_status),
+                                     _stream(stream))
+    _check(code, "sa_predict_mask_qk8")

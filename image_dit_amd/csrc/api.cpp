@@ -156,7 +156,7 @@ namespace sa {
 int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
                  const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                  int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status,
-                 void* stream) {
+                 void* stream, const Quant8* qz) {
     PredictShape s;
     const int st = predict_shape(p, &s);
     if (st != SA_OK) return st;
@@ -178,8 +178,13 @@ int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm,
     const int64_t n_groups = topcdf_groups(int64_t(s.B) * s.Hq, s.n_qb);
     const int64_t n_super = (n_groups + kSuperGroups - 1) / kSuperGroups;
     int32_t* super_tot = counts + s.rows + n_groups;
+    Quant8 z;
+    if (qz) {
+        z = *qz;
+        z.n_kt = (s.Nk + kKeyQuantRows - 1) / kKeyQuantRows;
+    }
     hipError_t e = launch_block_stats(q, k, perm, s, qbar, kbar, simq, simk, dev_status, super_tot, int(n_super),
-                                      hs);
+                                      qz ? &z : nullptr, hs);
     if (e != hipSuccess) return SA_ERR_HIP;
 
     TopCdfArgs a;
@@ -337,4 +342,21 @@ extern "C" int sa_sparse_attn_fwd_qk8(const uint8_t* q8, const float* q_scale, c
     f8.q8 = q8; f8.q_scale = q_scale; f8.k8 = k8; f8.k_scale = k_scale;
     return sparse_attn_fwd(nullptr, nullptr, v, perm_dev, o, p, row_ptr, col_idx, pv_skip, counters, dev_status,
                            stream, f8);
+}
+
+extern "C" int sa_predict_mask_qk8(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                                   const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr,
+                                   int32_t* col_idx, int64_t col_cap, uint8_t* q8, float* q_scale, uint8_t* k8,
+                                   float* k_scale, int32_t* dev_status, void* stream) {
+    const int st = validate_predict(p);
+    if (st != SA_OK) return st;
+    if (!q8 || !q_scale || !k8 || !k_scale) return SA_ERR_INVALID_ARGUMENT;
+    if (((reinterpret_cast<uintptr_t>(q8) | reinterpret_cast<uintptr_t>(k8)) & 7) ||
+        ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale)) & 3))
+        return SA_ERR_INVALID_ARGUMENT;
+    if (p->block_q > kQuantMaxBlock || !(p->block_k == kKeyQuantRows || p->block_k == 2 * kKeyQuantRows))
+        return SA_ERR_UNSUPPORTED;
+    Quant8 z{q8, q_scale, k8, k_scale, 0};
+    return predict_mask_impl(q, k, perm_dev, nullptr, p, ws, ws_bytes, row_ptr, col_idx, col_cap, nullptr, nullptr,
+                             nullptr, dev_status, stream, &z);
 }

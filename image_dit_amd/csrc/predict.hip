@@ -57,6 +57,7 @@ __device__ inline float wave_sum(float v) { return wave_reduce(v, [](float x, fl
 __device__ inline float wave_max(float v) { return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); }); }
 __device__ inline int wave_sum_i(int v) { return wave_reduce(v, [](int x, int y) { return x + y; }); }
 __device__ inline uint32_t wave_sum_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; }); }
+__device__ inline uint32_t wave_max_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return max(x, y); }); }
 
 // DPP lane move; lanes without a source (or in a disabled row) read 0.
 template <int CTRL, int ROW_MASK = 0xf>
@@ -109,7 +110,13 @@ __device__ inline void wave_lds_sync() {
 // reduced across the wave once at the end.  GATHER: q and k stay in the
 // original token order and row r of the reordered sequence is perm[r]; the
 // source rows of the next step are loaded while the current one is consumed.
-template <int D, bool GATHER>
+// QUANT: the same pass also finds each quantization block's largest magnitude
+// (a query block; a 64-row half of a key block); then a second pass over the
+// block's rows, read again while they are still in the caches, writes their
+// E4M3 codes with the rule of k_quant_fp8, so the codes and scales equal that
+// kernel's bit for bit.  (Keeping the block in registers instead, 190 VGPRs,
+// reads every row once but runs slower at two waves per SIMD.)
+template <int D, bool GATHER, bool QUANT>
 __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const int32_t* __restrict__ perm, int64_t N, int64_t Nk,
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
                                                      int n_qb, int n_kb, float* __restrict__ qbar,
                                                      float* __restrict__ kbar, float* __restrict__ simq,
                                                      float* __restrict__ simk, int32_t* dev_status,
-                                                     int32_t* super_tot, int n_super) {
+                                                     int32_t* super_tot, int n_super, Quant8 qz) {
     constexpr int CH = D / 8;
     constexpr int RPW = 64 / CH;   // rows per wave step
     constexpr int U = 8;           // steps in flight
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
             const int r = min(r0 + u * RPW + slot, len - 1);
             if constexpr (GATHER) {
                 const int32_t p = perm[t0 + r];
-                sr[u] = (p >= 0 && p < N) ? p : 0;  // an entry outside 0..N-1 reads row 0
+                sr[u] = (p >= 0 && p < N) ? p : -1;  // an entry outside 0..N-1 reads row 0
             } else {
                 sr[u] = r;
             }
@@ -158,38 +165,51 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
     float ax[8], au[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ax[e] = au[e] = 0.f;
+    uint32_t amx[2] = {0u, 0u};  // QUANT: largest |x| (bf16 pattern) of rows 0..63 and 64..127
+    // one row chunk (row r of the block; zeros past its end) into the sums
+    auto consume = [&](const uint4& raw, int r) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        if constexpr (QUANT) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7fffu, (w[c] >> 16) & 0x7fffu));
+            const int h = r >= 64 ? 1 : 0;  // blocks hold at most 128 rows
+            amx[h] = max(amx[h], m);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bf16x2 h = __builtin_bit_cast(bf16x2, w[c]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+        }
+        ss = group_sum<CH>(ss);
+        const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // zero rows (and padding) add nothing
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float lo = __uint_as_float(w[c] << 16);
+            const float hi = __uint_as_float(w[c] & 0xffff0000u);
+            ax[2 * c] += lo;
+            ax[2 * c + 1] += hi;
+            au[2 * c] = fmaf(lo, inv, au[2 * c]);
+            au[2 * c + 1] = fmaf(hi, inv, au[2 * c + 1]);
+        }
+    };
     for (int r0 = 0; r0 < len; r0 += U * RPW) {
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * RPW + slot;
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + int64_t(max(sr[u], 0)) * D) + ch;
+            u32x4 v;
             // streamed once: nontemporal, so the block rows do not displace cached data
-            const u32x4* p = reinterpret_cast<const u32x4*>(src + int64_t(sr[u]) * D) + ch;
-            const u32x4 v = __builtin_nontemporal_load(p);
+            // (QUANT reads them again right after: plain loads keep them cached)
+            if constexpr (QUANT) v = *p;
+            else v = __builtin_nontemporal_load(p);
             raw[u] = r < len ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
         }
         if (r0 + U * RPW < len) step_rows(r0 + U * RPW, sr);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-            float ss = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bf16x2 h = __builtin_bit_cast(bf16x2, w[c]);
-                ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
-            }
-            ss = group_sum<CH>(ss);
-            const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // zero rows (and padding) add nothing
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float lo = __uint_as_float(w[c] << 16);
-                const float hi = __uint_as_float(w[c] & 0xffff0000u);
-                ax[2 * c] += lo;
-                ax[2 * c + 1] += hi;
-                au[2 * c] = fmaf(lo, inv, au[2 * c]);
-                au[2 * c + 1] = fmaf(hi, inv, au[2 * c + 1]);
-            }
-        }
+        for (int u = 0; u < U; ++u) consume(raw[u], r0 + u * RPW + slot);
     }
     // sum the RPW row slots: lanes ch, ch+CH, ... hold the same columns
 #pragma unroll
@@ -212,6 +232,56 @@ __global__ __launch_bounds__(256) void k_block_stats(const uint16_t* __restrict_
         outm[0] = make_float4(ax[0] * inv_len, ax[1] * inv_len, ax[2] * inv_len, ax[3] * inv_len);
         outm[1] = make_float4(ax[4] * inv_len, ax[5] * inv_len, ax[6] * inv_len, ax[7] * inv_len);
         if (lane == 0) (is_q ? simq : simk)[local] = um2;
+    }
+    if constexpr (QUANT) {
+        // one quantization block per query block; a key block is one or two 64-row blocks
+        const int nh = is_q ? 1 : (len + kKeyQuantRows - 1) / kKeyQuantRows;
+        float inv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t mb = is_q ? max(wave_max_u(amx[0]), wave_max_u(amx[1])) : wave_max_u(amx[h]);
+            const float amax = __uint_as_float(mb << 16);
+            inv[h] = amax > 0.f ? 448.0f / amax : 0.f;
+            if (lane == 0 && h < nh) {
+                const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                if (is_q) qz.q_scale[local] = sc;
+                else qz.k_scale[bh * qz.n_kt + int64_t(j) * (bk / kKeyQuantRows) + h] = sc;
+            }
+        }
+        uint8_t* dst = (is_q ? qz.q8 : qz.k8) + (bh * Ns + (GATHER ? 0 : t0)) * D;
+        step_rows(0, sr);
+        for (int r0 = 0; r0 < len; r0 += U * RPW) {
+            uint4 raw[U];
+            int rows[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 v = *(reinterpret_cast<const u32x4*>(src + int64_t(max(sr[u], 0)) * D) + ch);
+                raw[u] = make_uint4(v.x, v.y, v.z, v.w);
+                rows[u] = sr[u];
+            }
+            if (r0 + U * RPW < len) step_rows(r0 + U * RPW, sr);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = r0 + u * RPW + slot;
+                if (r >= len) continue;
+                const float iv = inv[is_q ? 0 : (r >= 64 ? 1 : 0)];
+                const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                float y[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    y[2 * c] = __uint_as_float(w[c] << 16) * iv;
+                    y[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u) * iv;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+                if (rows[u] >= 0)
+                    *reinterpret_cast<uint2*>(dst + int64_t(rows[u]) * D + ch * 8) = make_uint2(uint32_t(lo), uint32_t(hi));
+            }
+        }
     }
 }
 
@@ -775,23 +845,29 @@ int64_t topcdf_groups(int64_t bh, int64_t n_qb) {
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk, int32_t* dev_status,
-                              int32_t* super_tot, int n_super, hipStream_t stream) {
+                              int32_t* super_tot, int n_super, const Quant8* qz, hipStream_t stream) {
     const int64_t qb = int64_t(s.B) * s.Hq * s.n_qb;
     const int64_t kb = int64_t(s.B) * s.Hkv * s.n_kb;
     const int64_t wgs = (qb + kb + 3) / 4;
     if (wgs > INT32_MAX || n_super > wgs) return hipErrorInvalidValue;
     const dim3 grid{unsigned(wgs), 1, 1};
-    auto go = [&](auto gather) {
-        constexpr bool G = decltype(gather)::value;
-        if (s.D == 128)
-            hipLaunchKernelGGL((k_block_stats<128, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
-                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status, super_tot, n_super);
-        else
-            hipLaunchKernelGGL((k_block_stats<64, G>), grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb,
-                               qb + kb, int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status, super_tot, n_super);
+    const Quant8 z = qz ? *qz : Quant8{};
+    if (qz && (s.bq > kQuantMaxBlock || s.bk % kKeyQuantRows != 0 || s.bk > 2 * kKeyQuantRows))
+        return hipErrorInvalidValue;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, q, k, perm, s.N, s.Nk, s.bq, s.bk, qb, qb + kb,
+                           int(s.n_qb), int(s.n_kb), qbar, kbar, simq, simk, dev_status, super_tot, n_super, z);
     };
-    if (perm) go(std::true_type{});
-    else go(std::false_type{});
+    auto go = [&](auto gather, auto quant) {
+        constexpr bool G = decltype(gather)::value;
+        constexpr bool Z = decltype(quant)::value;
+        if (s.D == 128) launch(k_block_stats<128, G, Z>);
+        else launch(k_block_stats<64, G, Z>);
+    };
+    if (perm && qz) go(std::true_type{}, std::true_type{});
+    else if (perm) go(std::true_type{}, std::false_type{});
+    else if (qz) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
     return hipGetLastError();
 }
 

@@ -58,10 +58,23 @@ struct TopCdfArgs {
     float scale;
 };
 
-// perm: token permutation (q and k in the original order), or null
+// FP8 codes and scales the block statistics pass writes as well (sa_predict_mask_qk8):
+// q8 [B,Hq,N,D] with q_scale [B,Hq,n_qb]; k8 [B,Hkv,N_k,D] with k_scale [B,Hkv,n_kt],
+// n_kt = ceil(N_k / kKeyQuantRows)
+struct Quant8 {
+    uint8_t* q8;
+    float* q_scale;
+    uint8_t* k8;
+    float* k_scale;
+    int64_t n_kt;
+};
+
+// perm: token permutation (q and k in the original order), or null; qz: null, or the
+// FP8 outputs to write in the same pass (block_q <= kQuantMaxBlock, block_k 64 or 128)
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const int32_t* perm, const PredictShape& s,
                               float* qbar, float* kbar, float* simq, float* simk,
-                              int32_t* dev_status, int32_t* super_tot, int n_super, hipStream_t stream);
+                              int32_t* dev_status, int32_t* super_tot, int n_super, const Quant8* qz,
+                              hipStream_t stream);
 hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream);
 // Number of TopCdf groups (8..16 consecutive query blocks of one head).
 int64_t topcdf_groups(int64_t bh, int64_t n_qb);
@@ -120,6 +133,6 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream);
 int predict_mask_impl(const uint16_t* q, const uint16_t* k, const int32_t* perm, const uint8_t* forced,
                       const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr, int32_t* col_idx,
                       int64_t col_cap, uint8_t* mask_out, float* sim_q, float* sim_k, int32_t* dev_status,
-                      void* stream);
+                      void* stream, const Quant8* qz = nullptr);
 
 }  // namespace sa

@@ -103,8 +103,10 @@ class SparseAttentionPath:
                  materialize=True, forced: Optional[np.ndarray] = None, qk_fp8=False):
         """forced: optional host block pattern [n_qb, n_kb] (nonzero = key block always kept by
         that query block, in every head), e.g. from ``sa_plan_tile_window``.
-        qk_fp8: take the QK products on per-block E4M3 codes (sa_quantize_fp8 +
-        sa_sparse_attn_fwd_qk8) instead of bf16."""
+        qk_fp8: take the QK products on per-block E4M3 codes instead of bf16: the gather form
+        writes them during the mask prediction (sa_predict_mask_qk8) and the attention reads
+        them (sa_sparse_attn_fwd_qk8); the materialising form quantizes the reordered copies
+        (sa_quantize_fp8) before the attention."""
         import torch
 
         self.cfg = cfg
@@ -143,6 +145,7 @@ class SparseAttentionPath:
         self.o_perm = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device) if materialize else None
         self.o = torch.empty((B, Hq, N, D), dtype=torch.float32, device=device)
         self.qk_fp8 = qk_fp8
+        self._quantized = False  # the codes of the last predict_gather are in place
         if qk_fp8:
             u8 = torch.uint8
             self.q8 = torch.empty((B, Hq, N, D), dtype=u8, device=device)
@@ -204,6 +207,12 @@ class SparseAttentionPath:
 
     # --- the fused form: the reorder is an index map inside the two kernels' loads ---
     def predict_gather(self, q, k, mask_out=None, sim_q=None, sim_k=None, stream=None):
+        if self.qk_fp8 and self.forced is None and mask_out is None and sim_q is None and sim_k is None:
+            # the prediction's pass over q and k also writes their E4M3 codes
+            L.sa_predict_mask_qk8(q, k, self.perm, self.mp, self.ws, self.row_ptr, self._cols(), self.q8,
+                                  self.q_scale, self.k8, self.k_scale, self.status[0:1], stream)
+            self._quantized = True
+            return
         if self.forced is not None:
             L.sa_predict_mask_ex(q, k, self.perm, self.forced, self.mp, self.ws, self.row_ptr, self._cols(),
                                  self.status[0:1], mask_out, sim_q, sim_k, stream)
@@ -213,7 +222,9 @@ class SparseAttentionPath:
 
     def attend_gather(self, q, k, v, stream=None):
         if self.qk_fp8:
-            self.quantize(q, k, self.perm, self.perm, stream)
+            if not self._quantized:  # codes not written by the last predict_gather
+                self.quantize(q, k, self.perm, self.perm, stream)
+            self._quantized = False
             self.attend_qk8_gather(v, stream)
             return
         L.sa_sparse_attn_fwd_gather(q, k, v, self.perm, self.o, self.ap, self.row_ptr, self.col_idx,

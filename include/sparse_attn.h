@@ -311,6 +311,21 @@ int sa_predict_mask_ex(const uint16_t* q, const uint16_t* k, const int32_t* perm
 int sa_quantize_fp8(const uint16_t* x, const int32_t* perm_dev, int32_t B, int32_t H, int64_t N,
                     int32_t D, int32_t block, uint8_t* codes, float* scales, void* stream);
 
+/* sa_predict_mask_ex (no forced pattern, no optional outputs) that also writes,
+ * in the same pass over Q and K, what sa_quantize_fp8 writes for them with the
+ * same perm_dev: q8 device uint8 [B,Hq,N,D] and q_scale device fp32
+ * [B,Hq,ceil(N/block_q)] (blocks of block_q rows), k8 device uint8 [B,Hkv,N_k,D]
+ * and k_scale device fp32 [B,Hkv,ceil(N_k/SA_FP8_KEY_ROWS)], bit for bit (for a
+ * perm_dev that is a permutation).  The inputs of sa_sparse_attn_fwd_qk8 thus
+ * come out of the mask prediction (SpargeAttn notes, sections 2.2 and 2.4: the
+ * prediction and the quantized QK path read the same Q and K blocks).  Needs
+ * block_q <= 128 and block_k = 64 or 128 (else SA_ERR_UNSUPPORTED); q8 and k8
+ * 8-byte aligned.  Other arguments, errors and outputs as in sa_predict_mask_ex. */
+int sa_predict_mask_qk8(const uint16_t* q, const uint16_t* k, const int32_t* perm_dev,
+                        const sa_mask_params* p, void* ws, size_t ws_bytes, int32_t* row_ptr,
+                        int32_t* col_idx, int64_t col_cap, uint8_t* q8, float* q_scale, uint8_t* k8,
+                        float* k_scale, int32_t* dev_status, void* stream);
+
 /* sa_sparse_attn_fwd (perm_dev NULL) or sa_sparse_attn_fwd_gather (perm_dev
  * non-NULL) with the QK products taken on FP8 operands (SpargeAttn notes,
  * section 2.4; the SageAttention idea on the gfx950 FP8 matrix cores): the

@@ -339,3 +339,45 @@ def test_fp8_full_size_sampled(name):
     log(f"[fp8 full] {name}: out_max={err_max:.3e} out_mean={err_sum / err_n:.3e} lam_far={lam_far}")
     assert err_max <= R.MAX_ABS and err_sum / err_n <= R.MEAN_ABS
     assert lam_far == 0
+
+
+# ------------------------------------------------------------------ quantization inside the prediction
+
+@pytest.mark.parametrize("name,fused", [("long_video_s", True), ("image_s", True), ("video_s", True),
+                                        ("causal_s_gqa", True), ("causal_s64_gqa_lam", True),
+                                        ("edge_n65_128x64_lam", True), ("edge_n129_128x128", True),
+                                        ("long_video_s", False), ("image_s", False)])
+def test_predict_mask_qk8_equals_separate_quantizer(name, fused):
+    """sa_predict_mask_qk8 writes the CSR of the plain prediction and, in the same pass, the
+    codes and scales sa_quantize_fp8 writes (which equal the oracle's), bit for bit; through
+    the permutation (fused) or on reordered copies (perm None)."""
+    w = CASES[name]
+    cfg = sa.config_from_workload(w)
+    q, k, _ = generate(w)
+    qd, kd = dev(q), dev(k)
+    path = sa.SparseAttentionPath(cfg, materialize=not fused, qk_fp8=True)
+    ref = sa.SparseAttentionPath(cfg, materialize=not fused, qk_fp8=True)
+    if fused:
+        perm = path.perm
+        qi, ki = qd, kd
+    else:
+        perm = None
+        path.permute(qd, kd, kd)
+        qi, ki = path.qp, path.kp
+    sa.sa_predict_mask_qk8(qi, ki, perm, path.mp, path.ws, path.row_ptr, path._cols(), path.q8, path.q_scale,
+                           path.k8, path.k_scale, path.status[0:1])
+    if fused:
+        sa.sa_predict_mask_gather(qd, kd, ref.perm, ref.mp, ref.ws, ref.row_ptr, ref._cols(), ref.status[0:1])
+    else:
+        sa.sa_predict_mask(qi, ki, ref.mp, ref.ws, ref.row_ptr, ref._cols(), ref.status[0:1])
+    ref.quantize(qi, ki, perm, perm)
+    torch.cuda.synchronize()
+    assert path.statuses()[0] == sa.SA_OK and ref.statuses()[0] == sa.SA_OK
+    ra, ca = path.csr_host()
+    rb, cb = ref.csr_host()
+    assert np.array_equal(ra, rb) and np.array_equal(ca, cb)
+    for a, b in ((path.q8, ref.q8), (path.k8, ref.k8)):
+        assert torch.equal(a, b)
+    for a, b in ((path.q_scale, ref.q_scale), (path.k_scale, ref.k_scale)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    log(f"[fp8] predict+quantize {name} fused={fused}: codes and scales equal, nnz={int(ra[-1])}")

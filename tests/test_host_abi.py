@@ -449,3 +449,23 @@ def test_qk8_rejects_bad_buffers():
     assert _qk8_code(p, v=None) == sa.SA_ERR_INVALID_ARGUMENT
     assert _qk8_code(p, q8=ctypes.c_void_p((1 << 20) + 8)) == sa.SA_ERR_INVALID_ARGUMENT
     assert _qk8_code(p, ks=ctypes.c_void_p((1 << 20) + 2)) == sa.SA_ERR_INVALID_ARGUMENT
+
+
+def _pq8_code(p, **ptrs):
+    args = dict(q=FAKE, k=FAKE, perm=None, ws=FAKE, row_ptr=FAKE, col_idx=FAKE, q8=FAKE, qs=FAKE, k8=FAKE, ks=FAKE,
+                status=FAKE)
+    args.update(ptrs)
+    return sa.lib().sa_predict_mask_qk8(args["q"], args["k"], args["perm"], ctypes.byref(p), args["ws"], 1 << 30,
+                                        args["row_ptr"], args["col_idx"], 100, args["q8"], args["qs"], args["k8"],
+                                        args["ks"], args["status"], None)
+
+
+def test_predict_mask_qk8_rejects_bad_arguments():
+    p = _mask_params(block_q=128, block_k=64)
+    assert _pq8_code(p, q8=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _pq8_code(p, ks=None) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _pq8_code(p, k8=ctypes.c_void_p((1 << 20) + 4)) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _pq8_code(p, qs=ctypes.c_void_p((1 << 20) + 2)) == sa.SA_ERR_INVALID_ARGUMENT
+    assert _pq8_code(_mask_params(block_q=128, block_k=32)) == sa.SA_ERR_UNSUPPORTED
+    assert _pq8_code(_mask_params(block_q=256, block_k=64)) == sa.SA_ERR_UNSUPPORTED
+    assert _pq8_code(_mask_params(B=0)) == sa.SA_ERR_INVALID_ARGUMENT
