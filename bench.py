@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
     ap.add_argument("--mode", default="path", choices=["path", "attn", "predict", "reorder", "copy", "ceilings"])
     ap.add_argument("--no-lambda", action="store_true", help="turn the workload's PV skip off")
+    ap.add_argument("--lam", type=float, default=None, help="override the workload's PV-skip threshold")
     ap.add_argument("--form", default="gather", choices=["gather", "materialize"],
                     help="reorder inside the kernels' loads (bf16 inputs) or as separate copies")
     ap.add_argument("--qk", default="bf16", choices=["bf16", "fp8"],
@@ -88,13 +89,10 @@ def attn_kernel_name(cfg, gather, fp8=False):
     """The attention kernel the attention entry point launches for this configuration."""
     if cfg.block_q == 16 and cfg.block_k == 16:
         return "k_flash_small"
-    if cfg.lam is not None and cfg.block_k == 128:
-        return "k_flash_mfma"
     g = "true" if gather else "false"
     f = "true" if fp8 else "false"
-    if cfg.lam is not None:
-        return f"k_flash_lam<{cfg.D}, {g}, {f}>"
-    return f"k_flash_dma<{cfg.D}, {1 if cfg.block_k == 64 else 2}, {g}, {f}>"
+    sub = 1 if cfg.block_k == 64 else 2
+    return f"k_flash_{'lam' if cfg.lam is not None else 'dma'}<{cfg.D}, {sub}, {g}, {f}>"
 
 
 def executed_flops(cfg, rp, ci, skip, groups):
@@ -281,6 +279,8 @@ def main():
         w = w.with_sparsity(args.sparsity)
     if args.no_lambda:
         w = dataclasses.replace(w, lam=None)
+    if args.lam is not None:
+        w = dataclasses.replace(w, lam=args.lam)
     if args.mode == "ceilings":
         print(json.dumps(ceilings(torch, w)))
         return

@@ -246,8 +246,7 @@ int sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
             (reinterpret_cast<uintptr_t>(f8.q_scale) | reinterpret_cast<uintptr_t>(f8.k_scale)) & 3)
             return SA_ERR_INVALID_ARGUMENT;
         const int64_t nk = p->n_keys > 0 ? p->n_keys : p->N;
-        if (p->D != 128 || p->block_q != 128 || !(p->block_k == 64 || (p->block_k == 128 && !(p->lambda > -INFINITY))))
-            return SA_ERR_UNSUPPORTED;
+        if (p->D != 128 || p->block_q != 128 || !(p->block_k == 64 || p->block_k == 128)) return SA_ERR_UNSUPPORTED;
         if ((nk + kKeyQuantRows - 1) / kKeyQuantRows >= kMaxKeyTiles) return SA_ERR_UNSUPPORTED;
         q = k = nullptr;
     } else if (!q || !k) {

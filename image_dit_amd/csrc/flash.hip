@@ -3,27 +3,21 @@
 // blocks outside the mask skip both QK^T and PV; section 2.3: PV skip when
 // the running-max gap of a row group is below lambda).
 //
-// k_flash_dma<D, SUB, GATHER>, k_flash_lam<D, GATHER>: the production kernels
-// for 64-key tiles without and with PV skip (k_flash_dma also runs 128-key
-// blocks without PV skip, as two 64-key tiles); see their comment.  GATHER
-// reads q, k, v through the token permutation and stores O back in the
-// original order.
+// k_flash_dma<D, SUB, GATHER, FP8>, k_flash_lam<D, SUB, GATHER, FP8>: the
+// kernels for 128-row query blocks without and with PV skip; 128-key blocks
+// (SUB = 2) run as two 64-key tiles, with one PV-skip decision per block in
+// k_flash_lam.  One workgroup of 4 wavefronts per query block; wavefront w owns
+// query rows 32w..32w+31 and is the PV-skip group.  Scores are computed
+// transposed, S^T = K Q^T, so that every accumulator a lane holds belongs to
+// ONE query row (lane & 31): row max/sum need no cross-lane work beyond one
+// exchange with lane ^ 32, and the output rescale is one scalar per lane.
+// O^T = V^T P^T reuses the exponentials as the B operand.  GATHER reads q, k,
+// v through the token permutation and stores O back in the original order;
+// FP8 takes the QK products on E4M3 codes with per-block scales.  See the
+// comments at the kernels.
 //
-// k_flash_mfma<D, BK>: one workgroup of 4 wavefronts per 128-row query block;
-// wavefront w owns query rows 32w..32w+31 and is the PV-skip group.  Scores
-// are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that
-// every accumulator a lane holds belongs to ONE query row (lane & 31): row
-// max/sum need no cross-lane work beyond one exchange with lane ^ 32, and the
-// output rescale is one scalar per lane.  O^T = V^T P^T reuses the score
-// registers directly as the B operand (the key order inside a 16-key MFMA
-// step only has to agree between the two operands).  K is staged row-major in
-// LDS (padded rows), V transposed (padded rows) so both MFMA operands are
-// contiguous LDS reads.
-//
-// k_flash_small<D>: the 16x16-block case (tiny workloads), plain fp32 ALU.
-//
-// The last two map rows through the permutation (when given) one load at a
-// time.
+// k_flash_small<D>: the 16x16-block case (tiny workloads), plain fp32 ALU; it
+// maps rows through the permutation (when given) one load at a time.
 #include <cmath>
 #include <type_traits>
 
@@ -86,218 +80,6 @@ __device__ inline int64_t src_row(const int32_t* perm, int64_t i, int64_t N) {
     if (!perm) return i;
     const int32_t r = perm[i];
     return (r >= 0 && r < N) ? r : 0;
-}
-
-template <int D, int BK>
-__global__ __launch_bounds__(256) void k_flash_mfma(FlashArgs a) {
-    constexpr int BQ = 128;
-    constexpr int KSTR = D + 8;   // bf16 per K row in LDS (16-byte pad: conflict-free 16-B reads)
-    constexpr int VSTR = BK + 4;  // bf16 per V^T row in LDS (8-byte pad)
-    constexpr int NT = D / 32;    // output tiles (32 dv each)
-    constexpr int KS = D / 16;    // MFMA k-steps over the head dim
-    constexpr int MT = BK / 32;   // score tiles (32 keys each)
-    constexpr int PS = BK / 16;   // MFMA k-steps over keys
-    __shared__ __align__(16) uint16_t Ks[BK * KSTR];
-    __shared__ __align__(16) uint16_t Vt[D * VSTR];
-
-    const int row = blockIdx.x;
-    const int qb = row % a.n_qb;
-    const int bh = row / a.n_qb;
-    const int hq = bh % a.Hq;
-    const int b = bh / a.Hq;
-    const int hk = hq / (a.Hq / a.Hkv);
-    const int64_t N = a.N;
-    const uint16_t* Qh = a.q + int64_t(bh) * N * D;
-    const int64_t Nk = a.Nk;
-    const uint16_t* Kh = a.k + (int64_t(b) * a.Hkv + hk) * Nk * D;
-    const uint16_t* Vh = a.v + (int64_t(b) * a.Hkv + hk) * Nk * D;
-    float* Oh = a.o + int64_t(bh) * N * D;
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int half = lane >> 5;
-    const int l32 = lane & 31;
-    const int64_t wrow0 = int64_t(qb) * BQ + wave * 32;
-    const int64_t qrow = wrow0 + l32;
-    const bool row_valid = qrow < N;
-    const bool wave_rows = wrow0 < N;
-
-    const int64_t qsrc = row_valid ? src_row(a.perm, qrow, N) : 0;
-    bf16x8_t qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4*>(Qh + qsrc * D + ks * 16 + half * 8);
-        qf[ks] = as_bf16x8(u);
-    }
-
-    floatx16 oacc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
-    float m_run = -INFINITY;
-    float l_part = 0.f;
-    const float c2 = a.scale * kLog2e;
-    const bool lam_on = a.lambda > -INFINITY;
-    const float lam2 = a.lambda * kLog2e;
-    int n_exec = 0, n_skip = 0;
-
-    int e0 = a.row_ptr[row];
-    int e1 = a.row_ptr[row + 1];
-    if (e1 > a.col_cap) {
-        if (tid == 0) *a.dev_status = SA_ERR_CAPACITY;
-        e1 = int(a.col_cap);
-    }
-    if (e0 < 0) {  // a malformed row_ptr: the row reads no entry
-        if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
-        e0 = e1 = 0;
-    }
-    for (int e = e0; e < e1; ++e) {
-        const int jblk = a.col_idx[e];
-        if (jblk < 0 || jblk >= a.n_kb) {  // uniform across the workgroup
-            if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
-            continue;
-        }
-        const int64_t kb0 = int64_t(jblk) * BK;
-        __syncthreads();  // previous block's LDS reads are done
-        // ---- K tile, row-major
-        constexpr int KCH = D / 8;
-#pragma unroll
-        for (int c = tid; c < BK * KCH; c += 256) {
-            const int rr = c / KCH, cc = c % KCH;
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (kb0 + rr < Nk) u = *reinterpret_cast<const uint4*>(Kh + src_row(a.perm, kb0 + rr, Nk) * D + cc * 8);
-            *reinterpret_cast<uint4*>(Ks + rr * KSTR + cc * 8) = u;
-        }
-        // ---- V tile, transposed through 4x4 register blocks
-        constexpr int DB4 = D / 4;
-#pragma unroll
-        for (int c = tid; c < (BK / 4) * DB4; c += 256) {
-            const int kb4 = c / DB4, db4 = c % DB4;
-            uint2 rv[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int64_t key = kb0 + kb4 * 4 + rr;
-                rv[rr] = key < Nk ? *reinterpret_cast<const uint2*>(Vh + src_row(a.perm, key, Nk) * D + db4 * 4)
-                                 : make_uint2(0, 0);
-            }
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int sh = (cc & 1) * 16;
-                const uint32_t x0 = ((cc < 2 ? rv[0].x : rv[0].y) >> sh) & 0xffffu;
-                const uint32_t x1 = ((cc < 2 ? rv[1].x : rv[1].y) >> sh) & 0xffffu;
-                const uint32_t x2 = ((cc < 2 ? rv[2].x : rv[2].y) >> sh) & 0xffffu;
-                const uint32_t x3 = ((cc < 2 ? rv[3].x : rv[3].y) >> sh) & 0xffffu;
-                *reinterpret_cast<uint2*>(Vt + (db4 * 4 + cc) * VSTR + kb4 * 4) =
-                    make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-            }
-        }
-        __syncthreads();
-        if (!wave_rows) {
-            if (a.pv_skip && lane == 0) a.pv_skip[int64_t(e) * 4 + wave] = 0;
-            continue;
-        }
-
-        // ---- S^T = K Q^T (keys x queries)
-        floatx16 sacc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Ks + (32 * mt + l32) * KSTR + ks * 16 + half * 8);
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-            }
-        }
-        // ---- online softmax for query row qrow (log2 domain)
-        float smax = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t key = kb0 + 32 * mt + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool ok = key < Nk && (!a.causal || key <= qrow);
-                const float s = ok ? sacc[mt][i] * c2 : -INFINITY;
-                sacc[mt][i] = s;
-                smax = fmaxf(smax, s);
-            }
-        smax = fmaxf(smax, __shfl_xor(smax, 32));
-        const float m_new = fmaxf(m_run, smax);
-        bool skip = false;
-        if (lam_on) {
-            float gap = (row_valid && smax > -INFINITY) ? smax - m_new : -INFINITY;
-            gap = wave_max(gap);
-            skip = gap < lam2;
-        }
-        const float msafe = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - msafe);
-        float psum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sacc[mt][i] - msafe);
-                sacc[mt][i] = p;
-                psum += p;
-            }
-        l_part = l_part * alpha + psum;
-        m_run = m_new;
-        if (a.pv_skip && lane == 0) a.pv_skip[int64_t(e) * 4 + wave] = skip ? 1 : 0;
-        if (skip) {
-            ++n_skip;
-            continue;
-        }
-        ++n_exec;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[t][i] *= alpha;
-        bf16x8_t pb[PS];
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-            for (int x = 0; x < 8; ++x) pb[ps][x] = (__bf16)sacc[ps >> 1][8 * (ps & 1) + x];
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int ps = 0; ps < PS; ++ps) {
-                const uint16_t* vp = Vt + (32 * t + l32) * VSTR + ps * 16 + 4 * half;
-                const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-                const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ps], oacc[t], 0, 0, 0);
-            }
-    }
-
-    // ---- epilogue: O / l
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
-    if (row_valid) {
-        const float inv = 1.0f / l_tot;  // l = 0 (no key) -> 0 * inf = NaN
-        if (l_tot == 0.f) *a.dev_status = SA_ERR_EMPTY_ROW;
-        float* orow = Oh + qsrc * D;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float4 v;
-                v.x = oacc[t][4 * g + 0] * inv;
-                v.y = oacc[t][4 * g + 1] * inv;
-                v.z = oacc[t][4 * g + 2] * inv;
-                v.w = oacc[t][4 * g + 3] * inv;
-                *reinterpret_cast<float4*>(orow + 32 * t + 8 * g + 4 * half) = v;
-            }
-    }
-    if (a.counters) {
-        if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)(e1 > e0 ? e1 - e0 : 0));
-        if (lane == 0 && wave_rows) {
-            atomicAdd(&a.counters[1], (unsigned long long)n_exec);
-            atomicAdd(&a.counters[2], (unsigned long long)n_skip);
-        }
-    }
 }
 
 // Small helpers of the pipelined kernels.
@@ -822,8 +604,8 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     }
 }
 
-// PV-skip variant of k_flash_dma (64-key tiles; the production path when
-// lambda is set).  Same LDS layouts, operand reads and online softmax.  The
+// PV-skip variant of k_flash_dma (the production path when lambda is set).
+// Same LDS layouts, operand reads and online softmax.  The
 // PV product of a tile is deferred by one iteration: during iteration t the
 // four waves fetch V of tile t-1 cooperatively (only if some wave kept the PV
 // of that tile; the need flags come through LDS), while the scores and
@@ -834,7 +616,18 @@ void k_flash_dma(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 // buffers; V needs one buffer.  The skip test of a 32-row group is one
 // ballot: skip when no valid row's block maximum comes within lambda of its
 // new running maximum.
-template <int D, bool GATHER, bool FP8>
+//
+// SUB = 2: 128-key blocks as two 64-key tiles with one decision per block, as
+// the PV-skip rule defines it (the block's row maximum against the running
+// maximum after the whole block).  The first half is scored and added to m and
+// l as usual and its P kept pending undecided; the second half decides for
+// both.  The first half's V is therefore fetched whatever the decision (during
+// the second half's iteration), and its PV product is applied there, after
+// the decision, or dropped.  A skipped block never raises a valid row's
+// maximum, so dropping needs no rescale; a kept one applies O <- aA O + PA VA,
+// then (one iteration later) O <- aB O + PB VB, which equals the block update
+// with P taken against the maximum after the block.
+template <int D, int SUB, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                  uint8_t* __restrict__ pv_skip) {
@@ -912,12 +705,13 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         if (tid == 0) *a.dev_status = SA_ERR_INVALID_ARGUMENT;
         e0 = e1 = 0;
     }
-    const int nt = e1 > e0 ? e1 - e0 : 0;
+    const int ne = e1 > e0 ? e1 - e0 : 0;  // CSR entries (key blocks) of the row
+    const int nt = ne * SUB;                // 64-key tiles
 
     auto tile_key0 = [&](int t) -> int {
-        const int j = col_idx[e0 + t];
+        const int j = col_idx[e0 + t / SUB];
         if (j < 0 || j >= a.n_kb) return -1;
-        return j * BK;
+        return j * (BK * SUB) + (t % SUB) * BK;
     };
     const TileLane<D> tl(wave, lane);
     const int4v rP = head_desc(a.perm, uint32_t(N) * 4u);
@@ -1031,18 +825,18 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         }
     };
 
-    // column indices of tiles 0 .. 2*kColChunk-1 (published by the barrier before the
+    // column indices of entries 0 .. 2*kColChunk-1 (published by the barrier before the
     // loop); later chunks are DMA'd by wave 0 one chunk ahead.  No scalar loads stay in
     // the loop: an outstanding one would make every LDS-operand wait a full lgkmcnt(0).
     {
         constexpr int PER = 2 * kColChunk / 256;
         int cv[PER];
 #pragma unroll
-        for (int x = 0; x < PER; ++x) cv[x] = tid + 256 * x < nt ? col_idx[e0 + tid + 256 * x] : -1;
+        for (int x = 0; x < PER; ++x) cv[x] = tid + 256 * x < ne ? col_idx[e0 + tid + 256 * x] : -1;
 #pragma unroll
         for (int x = 0; x < PER; ++x) (&colc[0][0])[tid + 256 * x] = cv[x];
     }
-    const int4v rC = head_desc(col_idx + (nt > 0 ? e0 : 0), uint32_t(nt) * 4u);
+    const int4v rC = head_desc(col_idx + (ne > 0 ? e0 : 0), uint32_t(ne) * 4u);
     // kr: source rows of the next K tile to fetch (t+2 during iteration t);
     // vr: those of tile t-1, whose V may be fetched during iteration t
     Rows kr, vr;
@@ -1091,23 +885,29 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     prefetch_k(0);
     int kbuf = 0;  // t % 3, also the need slot of tile t
     uint32_t need_prev = 0u;  // the need flags of tile t-1, read after the last barrier
-    uint64_t skipm = 0ull;    // bit i: PV of tile t - t % 64 + i skipped (this wave's group)
+    uint64_t skipm = 0ull;    // bit i: PV of entry et - et % 64 + i skipped (this wave's group)
+    float mx_first = -INFINITY;  // SUB = 2: the block's first-half row maximum
     for (int t = 0; t < nt; ++t) {
         const int kb0 = kc;
-        // V of tile t-1 first (so waiting for it leaves the K prefetch in flight)
+        const int et = t / SUB;                        // CSR entry of tile t
+        const bool first = SUB == 2 && (t & 1) == 0;   // first half of a 128-key block
+        const bool second = SUB == 2 && (t & 1) == 1;  // ... the half that decides
+        // V of tile t-1 first (so waiting for it leaves the K prefetch in flight); the
+        // first half of a block is fetched whatever the decision
         const uint32_t need_s = __builtin_amdgcn_readfirstlane(need_prev);
-        const bool vprev = t > 0 && need_s != 0u;
-        // raw column index of tile t+5 (LDS), checked and turned into a key at the end
-        // of the iteration
-        int c5v = colc[((t + 5) / kColChunk) & 1][(t + 5) % kColChunk];  // stale past the row's end
-        // the chunk after next: tiles t+kColChunk.., into the buffer of the chunk that
-        // ended with tile t-1 (its last read was in iteration t-6); issued before the
-        // V and K tiles so the waits below cover it
-        if (wave == 0 && t > 0 && (t % kColChunk) == 0 && t + kColChunk < nt) {
-            const uint32_t cl = lds_addr(&colc[((t / kColChunk) + 1) & 1][0]);
+        const bool vprev = second || (t > 0 && need_s != 0u);
+        // raw column index of the entry of tile t+5 (LDS), checked and turned into a key
+        // at the end of the iteration
+        const int e5 = (t + 5) / SUB;
+        int c5v = colc[(e5 / kColChunk) & 1][e5 % kColChunk];  // stale past the row's end
+        // the chunk after next: entries et+kColChunk.., into the buffer of the chunk that
+        // ended with entry et-1 (its last read was at least five tiles ago); issued before
+        // the V and K tiles so the waits below cover it
+        if (wave == 0 && t % SUB == 0 && et > 0 && (et % kColChunk) == 0 && et + kColChunk < ne) {
+            const uint32_t cl = lds_addr(&colc[((et / kColChunk) + 1) & 1][0]);
 #pragma unroll
             for (int h = 0; h < kColChunk / 256; ++h)
-                dma16_at(rC, cl + uint32_t(h * 1024), uint32_t(t + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
+                dma16_at(rC, cl + uint32_t(h * 1024), uint32_t(et + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
         }
         // prefetches past the row's end (key -1) read zeros into buffers nobody reads,
         // so they need no condition
@@ -1172,8 +972,11 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
             const float smax = max2f(lo, hi) * f;
             const float m_new = max2f(m_run, smax);
+            // the block's row maximum: this tile's, or (second half) both halves'
+            const float bmax = second ? max2f(mx_first, smax) : smax;
+            if (first) mx_first = smax;
             // NaN (no key yet) and -inf gaps never reach lambda
-            const bool skip = __builtin_amdgcn_ballot_w64(row_valid && smax - m_new >= lam_raw) == 0ull;
+            const bool skip = __builtin_amdgcn_ballot_w64(row_valid && bmax - m_new >= lam_raw) == 0ull;
             alpha = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;  // 0 when m_run = -inf
             m_run = m_new;
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
@@ -1203,19 +1006,22 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
             for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
             l_part = fmaf(l_part, alpha, ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
-            if (skip) {
-                skipm |= 1ull << (t & 63);
+            if (first) {
+                my_need = 1;  // undecided: kept pending until the second half decides
+            } else if (skip) {
+                skipm |= 1ull << (et & 63);
                 ++n_skip;
             } else {
                 ++n_exec;
                 my_need = 1;
             }
         }
-        // PV of tile t-1 once every wave's part of its V tile has landed
+        // PV of tile t-1 once every wave's part of its V tile has landed (the second
+        // half drops its block's first-half product when the block is skipped)
         if (vprev) {
             dma_wait<DK>();  // only the K DMAs issued after it may still be in flight
             tile_barrier();
-            if (pend) apply_pending();
+            if (pend && (!second || my_need)) apply_pending();
         }
         // tile t becomes the pending one
         pend = my_need != 0;
@@ -1230,9 +1036,9 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             palpha = alpha;
         }
         if (lane == 0) need[kbuf][wave] = uint8_t(my_need);
-        // the skip flags of 64 tiles leave in one store (lane i: tile t - t % 64 + i)
-        if (pv_skip && ((t & 63) == 63 || t == nt - 1)) {
-            if (lane <= (t & 63)) pv_skip[int64_t(e0 + (t & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
+        // the skip flags of 64 entries leave in one store (lane i: entry et - et % 64 + i)
+        if (pv_skip && (t % SUB) == SUB - 1 && ((et & 63) == 63 || t == nt - 1)) {
+            if (lane <= (et & 63)) pv_skip[int64_t(e0 + (et & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
             skipm = 0ull;
         }
         // K of tile t+1 and the source rows of tile t+4 have landed (K of t+2
@@ -1253,7 +1059,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         // compiler from moving the read-first-lane, and its wait, up to the read)
         asm volatile("" : "+v"(c5v));
         const int c5 = __builtin_amdgcn_readfirstlane(c5v);
-        k4 = (t + 5 >= nt || c5 < 0 || c5 >= a.n_kb) ? -1 : c5 * BK;
+        k4 = (t + 5 >= nt || c5 < 0 || c5 >= a.n_kb) ? -1 : c5 * (BK * SUB) + ((t + 5) % SUB) * BK;
     }
     dma_wait<0>();  // no LDS write may land after the workgroup ends
     if (nt > 0 && __builtin_amdgcn_readfirstlane(need_prev) != 0u) {
@@ -1284,7 +1090,7 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
     }
     if (a.counters) {
-        if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)nt);
+        if (tid == 0) atomicAdd(&a.counters[0], (unsigned long long)ne);
         if (lane == 0 && wave_rows) {
             atomicAdd(&a.counters[1], (unsigned long long)n_exec);
             atomicAdd(&a.counters[2], (unsigned long long)n_skip);
@@ -1424,47 +1230,30 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t stream) {
     const bool lam_on = a.lambda > -INFINITY;
     const dim3 grid{unsigned(rows), 1, 1};
     const dim3 block{256, 1, 1};
+    const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
+    const bool G = a.perm != nullptr;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip); };
     if (a.q8) {
-        // FP8 QK path: head dim 128, 128-row query blocks, 64-key tiles (128-key
-        // blocks without PV skip); the caller has checked the shape
-        if (a.D != 128 || a.bq != 128 || (a.bk == 128 && lam_on)) return hipErrorInvalidValue;
+        // FP8 QK path: head dim 128, 128-row query blocks; the caller has checked the shape
+        if (a.D != 128 || a.bq != 128 || !(a.bk == 64 || a.bk == 128)) return hipErrorInvalidValue;
         if (a.n_kt != (a.Nk + 63) / 64 || a.n_kt >= kMaxKeyTiles) return hipErrorInvalidValue;
-        const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
-        const bool G = a.perm != nullptr;
-        if (a.bk == 64 && lam_on) {
-            if (G) hipLaunchKernelGGL((k_flash_lam<128, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            else hipLaunchKernelGGL((k_flash_lam<128, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-        } else if (a.bk == 64) {
-            if (G) hipLaunchKernelGGL((k_flash_dma<128, 1, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            else hipLaunchKernelGGL((k_flash_dma<128, 1, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-        } else {
-            if (G) hipLaunchKernelGGL((k_flash_dma<128, 2, true, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            else hipLaunchKernelGGL((k_flash_dma<128, 2, false, true>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-        }
+        if (lam_on && a.bk == 64) G ? go(k_flash_lam<128, 1, true, true>) : go(k_flash_lam<128, 1, false, true>);
+        else if (lam_on) G ? go(k_flash_lam<128, 2, true, true>) : go(k_flash_lam<128, 2, false, true>);
+        else if (a.bk == 64) G ? go(k_flash_dma<128, 1, true, true>) : go(k_flash_dma<128, 1, false, true>);
+        else G ? go(k_flash_dma<128, 2, true, true>) : go(k_flash_dma<128, 2, false, true>);
     } else if (a.bq == 16 && a.bk == 16) {
         if (a.D == 128) hipLaunchKernelGGL(k_flash_small<128>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(k_flash_small<64>, grid, block, 0, stream, a);
-    } else if (a.bk == 128 && lam_on) {
-        // a PV-skip decision needs all 128 keys of a block at once
-        if (a.D == 128) hipLaunchKernelGGL((k_flash_mfma<128, 128>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((k_flash_mfma<64, 128>), grid, block, 0, stream, a);
+    } else if (a.D == 128) {
+        if (lam_on && a.bk == 64) G ? go(k_flash_lam<128, 1, true, false>) : go(k_flash_lam<128, 1, false, false>);
+        else if (lam_on) G ? go(k_flash_lam<128, 2, true, false>) : go(k_flash_lam<128, 2, false, false>);
+        else if (a.bk == 64) G ? go(k_flash_dma<128, 1, true, false>) : go(k_flash_dma<128, 1, false, false>);
+        else G ? go(k_flash_dma<128, 2, true, false>) : go(k_flash_dma<128, 2, false, false>);
     } else {
-        const dim3 pgrid{unsigned((rows + 7) / 8 * 8), 1, 1};
-        auto go = [&](auto gather) {
-            constexpr bool G = decltype(gather)::value;
-            if (a.bk == 64 && lam_on) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_lam<128, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_lam<64, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            } else if (a.bk == 64) {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 1, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 1, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            } else {
-                if (a.D == 128) hipLaunchKernelGGL((k_flash_dma<128, 2, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-                else hipLaunchKernelGGL((k_flash_dma<64, 2, G, false>), pgrid, block, 0, stream, a, a.row_ptr, a.col_idx, a.pv_skip);
-            }
-        };
-        if (a.perm) go(std::true_type{});
-        else go(std::false_type{});
+        if (lam_on && a.bk == 64) G ? go(k_flash_lam<64, 1, true, false>) : go(k_flash_lam<64, 1, false, false>);
+        else if (lam_on) G ? go(k_flash_lam<64, 2, true, false>) : go(k_flash_lam<64, 2, false, false>);
+        else if (a.bk == 64) G ? go(k_flash_dma<64, 1, true, false>) : go(k_flash_dma<64, 1, false, false>);
+        else G ? go(k_flash_dma<64, 2, true, false>) : go(k_flash_dma<64, 2, false, false>);
     }
     return hipGetLastError();
 }

@@ -336,9 +336,8 @@ int sa_predict_mask_qk8(const uint16_t* q, const uint16_t* k, const int32_t* per
  * sa_sparse_attn_fwd.  q8: device uint8 [B,Hq,N,D] with q_scale device fp32
  * [B,Hq,ceil(N/block_q)]; k8: device uint8 [B,Hkv,N_k,D] with k_scale device
  * fp32 [B,Hkv,ceil(N_k/SA_FP8_KEY_ROWS)], both as written by sa_quantize_fp8
- * (with the same perm_dev).  Needs D = 128, block_q = 128, and block_k = 64,
- * or block_k = 128 with lambda off; ceil(N_k/64) below 4096 (else
- * SA_ERR_UNSUPPORTED).  q8 and k8 16-byte aligned.  Other arguments, errors
+ * (with the same perm_dev).  Needs D = 128, block_q = 128, block_k = 64 or
+ * 128 and ceil(N_k/64) below 4096 (else SA_ERR_UNSUPPORTED).  q8 and k8 16-byte aligned.  Other arguments, errors
  * and outputs as in sa_sparse_attn_fwd / sa_sparse_attn_fwd_gather. */
 int sa_sparse_attn_fwd_qk8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                            const float* k_scale, const uint16_t* v, const int32_t* perm_dev, float* o,

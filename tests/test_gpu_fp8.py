@@ -51,6 +51,9 @@ CASES = {
     "edge_n65_128x64_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 65), block_k=64, lam=-8.0, seed=304),
     "edge_n129_128x128": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 129), seed=305),
     "edge_n1_128x64_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 1), block_k=64, lam=-8.0, seed=306),
+    # PV skip on 128-key blocks (one decision per block)
+    "image_s_lam": rep(_im, Hq=3, Hkv=3, latent=(1, 20, 37), lam=-8.0, seed=308),
+    "edge_n193_128x128_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 193), lam=-8.0, seed=309),
 }
 
 

@@ -36,6 +36,8 @@ FULL_W["max_blocks_causal"] = dataclasses.replace(CONFIGS["causal_long"], Hq=2, 
 # the video workload with keys and values on a grid of half its width (12514 keys for 24802
 # queries; the first key frame and the key text are the sinks); materialising form only
 FULL_W["video_kv"] = dataclasses.replace(CONFIGS["video"], latent_k=(16, 32, 24), sink_front=32 * 24, seed=83)
+# the image workload with PV skip on its 128-key blocks (a whole-block decision per 32-row group)
+FULL_W["image_lam"] = dataclasses.replace(CONFIGS["image"], lam=-8.0, seed=84)
 FULL = list(FULL_W)
 FULL_GATHER = [name for name in FULL if FULL_W[name].N_k == FULL_W[name].N]
 

@@ -83,6 +83,11 @@ EDGE = {
                                 seed=209),
     "edge_causal_n129_128x128": rep(_ca, Hq=2, Hkv=1, latent=(1, 1, 129), window_tokens=64, seed=210),
     "edge_d64_n65_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 65), D=64, block_k=64, lam=-8.0, seed=211),
+    # PV skip on 128-key blocks (one decision per block over its two 64-key tiles): causal
+    # with a window, d = 64, and a last block whose second tile lies past the end
+    "causal_s_lam": rep(_ca, Hq=4, Hkv=2, latent=(1, 1, 2000), window_tokens=512, lam=-8.0, seed=212),
+    "image_s_d64_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 20, 37), D=64, lam=-8.0, seed=213),
+    "edge_n193_128x128_lam": rep(_im, Hq=2, Hkv=2, latent=(1, 1, 193), lam=-8.0, seed=214),
 }
 SMALL.update(EDGE)
 

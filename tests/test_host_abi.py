@@ -430,7 +430,7 @@ def _qk8_code(p, perm=None, **ptrs):
 @pytest.mark.parametrize("kw,code", [
     (dict(D=64), sa.SA_ERR_UNSUPPORTED),                          # FP8 QK path: head dim 128 only
     (dict(block_q=16, block_k=16, D=128), sa.SA_ERR_UNSUPPORTED),
-    (dict(block_k=128, lam=-8.0), sa.SA_ERR_UNSUPPORTED),         # 128-key blocks: lambda off only
+    (dict(block_k=32), sa.SA_ERR_UNSUPPORTED),
     (dict(N=4096 * 64), sa.SA_ERR_UNSUPPORTED),                   # key-tile scales must fit the table
     (dict(lam=0.5), sa.SA_ERR_INVALID_ARGUMENT),
 ])
