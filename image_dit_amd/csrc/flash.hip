@@ -887,6 +887,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     uint32_t need_prev = 0u;  // the need flags of tile t-1, read after the last barrier
     uint64_t skipm = 0ull;    // bit i: PV of entry et - et % 64 + i skipped (this wave's group)
     float mx_first = -INFINITY;  // SUB = 2: the block's first-half row maximum
+    int refill_t = kColChunk * SUB;  // next tile that starts a column chunk
+    int flush_t = 64 * SUB - 1;      // next tile whose entry ends a run of 64 skip flags
     for (int t = 0; t < nt; ++t) {
         const int kb0 = kc;
         const int et = t / SUB;                        // CSR entry of tile t
@@ -898,16 +900,20 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         const bool vprev = second || (t > 0 && need_s != 0u);
         // raw column index of the entry of tile t+5 (LDS), checked and turned into a key
         // at the end of the iteration
-        const int e5 = (t + 5) / SUB;
-        int c5v = colc[(e5 / kColChunk) & 1][e5 % kColChunk];  // stale past the row's end
+        // (the two chunks are one ring of 2 kColChunk entries)
+        int c5v = (&colc[0][0])[((t + 5) / SUB) & (2 * kColChunk - 1)];  // stale past the row's end
         // the chunk after next: entries et+kColChunk.., into the buffer of the chunk that
         // ended with entry et-1 (its last read was at least five tiles ago); issued before
         // the V and K tiles so the waits below cover it
-        if (wave == 0 && t % SUB == 0 && et > 0 && (et % kColChunk) == 0 && et + kColChunk < ne) {
-            const uint32_t cl = lds_addr(&colc[((et / kColChunk) + 1) & 1][0]);
+        if (t == refill_t) {
+            refill_t += kColChunk * SUB;
+            if (wave == 0 && et + kColChunk < ne) {
+                const uint32_t cl = lds_addr(&colc[((et / kColChunk) + 1) & 1][0]);
 #pragma unroll
-            for (int h = 0; h < kColChunk / 256; ++h)
-                dma16_at(rC, cl + uint32_t(h * 1024), uint32_t(et + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
+                for (int h = 0; h < kColChunk / 256; ++h)
+                    dma16_at(rC, cl + uint32_t(h * 1024),
+                             uint32_t(et + kColChunk + h * 256) * 4u + uint32_t(lane) * 16u);
+            }
         }
         // prefetches past the row's end (key -1) read zeros into buffers nobody reads,
         // so they need no condition
@@ -1037,8 +1043,10 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
         }
         if (lane == 0) need[kbuf][wave] = uint8_t(my_need);
         // the skip flags of 64 entries leave in one store (lane i: entry et - et % 64 + i)
-        if (pv_skip && (t % SUB) == SUB - 1 && ((et & 63) == 63 || t == nt - 1)) {
-            if (lane <= (et & 63)) pv_skip[int64_t(e0 + (et & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
+        if (t == flush_t || t == nt - 1) {
+            flush_t += 64 * SUB;
+            if (pv_skip && lane <= (et & 63))
+                pv_skip[int64_t(e0 + (et & ~63) + lane) * 4 + wave] = uint8_t((skipm >> lane) & 1ull);
             skipm = 0ull;
         }
         // K of tile t+1 and the source rows of tile t+4 have landed (K of t+2
