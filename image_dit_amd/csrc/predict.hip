@@ -56,7 +56,6 @@ __device__ inline T wave_reduce(T v, F op) {
 __device__ inline float wave_sum(float v) { return wave_reduce(v, [](float x, float y) { return x + y; }); }
 __device__ inline float wave_max(float v) { return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); }); }
 __device__ inline int wave_sum_i(int v) { return wave_reduce(v, [](int x, int y) { return x + y; }); }
-__device__ inline uint32_t wave_sum_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; }); }
 __device__ inline uint32_t wave_max_u(uint32_t v) { return wave_reduce(v, [](uint32_t x, uint32_t y) { return max(x, y); }); }
 
 // DPP lane move; lanes without a source (or in a disabled row) read 0.
@@ -354,42 +353,68 @@ __device__ inline bool is_candidate(uint32_t key) { return key != 0u && key < kF
 __device__ inline int digit_shift(int lv) { return lv == 3 ? 0 : 22 - 8 * lv; }
 __device__ inline int digit_width(int lv) { return lv == 3 ? 6 : 8; }
 
+// Histogram bins hold a count and a fixed-point mass together: count in the
+// high word, mass in the low word.  A bin's mass is a sum of candidate masses,
+// below 2^32 (see kFix), so one 64-bit add updates both without a carry
+// between them.
+struct BinHit {
+    uint32_t digit;        // the bin where the target is reached
+    uint32_t cnt_before;   // candidates in the bins above it
+    uint32_t mass_before;  // their mass
+    uint32_t bin_cnt;      // candidates in the bin
+    uint32_t bin_mass;     // their mass
+};
+
 // In the histogram scan lane l owns digits 255-4l .. 252-4l (highest first).
 // Finds the first digit, in descending order, at which base + the inclusive
-// cumulative bin value reaches `target`; returns false when none does, else
-// the digit and the cumulative value of the digits above it.
-__device__ inline bool scan_digits(const uint32_t* hist, uint32_t base, uint32_t target, int lane,
-                                   uint32_t& digit, uint32_t& before) {
-    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[63 - lane];
-    const uint32_t v[4] = {h4.w, h4.z, h4.y, h4.x};  // descending digits
-    const uint32_t lt = v[0] + v[1] + v[2] + v[3];
-    const uint32_t incl = wave_incl_scan(lt);
-    const unsigned long long hit = __ballot(base + incl >= target);
+// cumulative mass (BY_MASS) or count reaches `target`; returns false when none
+// does.
+template <bool BY_MASS>
+__device__ inline bool scan_bins(const unsigned long long* hist, uint32_t base, uint32_t target, int lane,
+                                 BinHit& h) {
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
+    const uint4 lo = h4[0], hi = h4[1];  // digits 252-4l, 253-4l | 254-4l, 255-4l
+    const uint32_t m[4] = {hi.z, hi.x, lo.z, lo.x};  // descending digits
+    const uint32_t c[4] = {hi.w, hi.y, lo.w, lo.y};
+    const uint32_t lm = m[0] + m[1] + m[2] + m[3];
+    const uint32_t lc = c[0] + c[1] + c[2] + c[3];
+    const uint32_t im = wave_incl_scan(lm);
+    const uint32_t ic = wave_incl_scan(lc);
+    const unsigned long long hit = __ballot(base + (BY_MASS ? im : ic) >= target);
     if (hit == 0ull) return false;
     const int hl = __ffsll(static_cast<long long>(hit)) - 1;
-    uint32_t run = incl - lt, pos = 3, bef = run;
+    uint32_t rm = im - lm, rc = ic - lc;
+    uint32_t pos = 3, bm = rm, bc = rc, hm = m[3], hc = c[3];
     bool done = false;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        if (!done && base + run + v[t] >= target) {
+        if (!done && base + (BY_MASS ? rm + m[t] : rc + c[t]) >= target) {
             pos = t;
-            bef = run;
+            bm = rm;
+            bc = rc;
+            hm = m[t];
+            hc = c[t];
             done = true;
         }
-        run += v[t];
+        rm += m[t];
+        rc += c[t];
     }
-    digit = __builtin_amdgcn_readlane(255u - 4u * uint32_t(lane) - pos, hl);
-    before = __builtin_amdgcn_readlane(bef, hl);
+    h.digit = __builtin_amdgcn_readlane(255u - 4u * uint32_t(lane) - pos, hl);
+    h.cnt_before = __builtin_amdgcn_readlane(bc, hl);
+    h.mass_before = __builtin_amdgcn_readlane(bm, hl);
+    h.bin_cnt = __builtin_amdgcn_readlane(hc, hl);
+    h.bin_mass = __builtin_amdgcn_readlane(hm, hl);
     return true;
 }
 
-// Histogram of digit `lv` over the candidate keys that carry prefix `pref`
-// above it, in this wavefront's 256-bin LDS array: counts, or fixed-point
-// masses when MASS.
-template <bool MASS>
-__device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pref, uint32_t* hist, int lane) {
+// Histogram (count and mass per bin) of digit `lv` over the candidate keys
+// that carry prefix `pref` above it, in this wavefront's 256-bin LDS array.
+__device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pref, unsigned long long* hist,
+                                  int lane) {
     const int sh = digit_shift(lv), w = digit_width(lv);
-    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+    h4[lane] = make_uint4(0, 0, 0, 0);
+    h4[lane + 64] = make_uint4(0, 0, 0, 0);
     wave_lds_sync();
     for (int q = lane; 4 * q < nv; q += 64) {
         const uint4 x = row4[q];
@@ -400,11 +425,19 @@ __device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pr
             // forced keys never match a prefix
             if (kk != 0u && (kk >> (sh + w)) == pref) {
                 const uint32_t d = (kk >> sh) & ((1u << w) - 1u);
-                atomicAdd(&hist[d], MASS ? key_mass(kk) : 1u);
+                atomicAdd(&hist[d], (1ull << 32) | key_mass(kk));
             }
         }
     }
     wave_lds_sync();
+}
+
+// Lowest key whose digits down to level lv are `pref`, minus one: keeping the
+// candidates above it keeps that whole bin and everything above it (candidate
+// keys are at least 1, so a bin starting at 0 keeps every candidate).
+__device__ inline uint32_t bin_floor(uint32_t pref, int lv) {
+    const uint32_t lb = pref << digit_shift(lv);
+    return lb == 0u ? 0u : lb - 1u;
 }
 
 // One query block (row i of head bh) on one wavefront, its compressed scores
@@ -412,12 +445,11 @@ __device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pr
 // lane takes four consecutive key blocks per step.  Candidates are ordered by
 // probability descending, ties by block index ascending; TopCdf keeps the
 // shortest prefix whose mass reaches tau, the floor keeps at least `extra`
-// candidates.  Both cut points are found exactly with four histogram passes
-// over the radix digits of the keys (the TopCdf search carries the mass per
-// bin, the floor search the count), so no sort is needed.  Returns the row's
-// kept count.
+// candidates.  Both cut points are found exactly with at most four histogram
+// passes each over the radix digits of the keys, so no sort is needed.
+// Returns the row's kept count.
 __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint32_t* row, const uint32_t* colf,
-                          uint32_t* hS, int lane) {
+                          unsigned long long* hS, int lane) {
     const RowGeom g = row_geom(a, i);
     const int64_t grow = int64_t(bh) * a.n_qb + i;
     // low-similarity query blocks and sink rows keep their whole valid row
@@ -492,70 +524,83 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
         c_on = true;
         T = max(1u, uint32_t(ceil(a.tau_d * kFixD)));
     }
-    // floor: the extra-th largest key and how many of its ties are needed
-    uint32_t x_pref = 0, x_rem = uint32_t(extra);
+    // Both cut points are found by descending the radix digits of the keys,
+    // one count+mass histogram per level.  The floor search (the extra-th
+    // candidate in order) stops at the first bin all of whose candidates it
+    // needs; the TopCdf search (the candidate at which the cumulative mass
+    // reaches T) stops at the first bin that holds one candidate.  Each ends as
+    // a threshold: every candidate above `thr` is kept, plus the first `quota`
+    // (lowest indices) of those equal to it, which only a search that reaches
+    // the last digit with ties left needs.  While the two searches follow the
+    // same digits they share the histogram.
     const bool x_on = extra > 0 && extra < n_cand;
-    if (x_on) {
-        for (int lv = 0; lv < 4; ++lv) {
-            digit_hist<false>(row4, nv, lv, x_pref, hS, lane);
-            uint32_t d = 0, bef = 0;
-            scan_digits(hS, 0u, x_rem, lane, d, bef);
-            x_rem -= bef;
-            x_pref = (x_pref << digit_width(lv)) | d;
+    uint32_t f_pref = 0, f_rem = uint32_t(extra), f_mass = 0, f_thr = 0, f_quota = 0;
+    uint32_t c_pref = 0, c_acc = 0, c_cnt = 0, c_thr = 0, c_quota = 0;
+    int c_lv = 0;
+    bool c_done = !c_on, c_found = true;
+    // one TopCdf level on the histogram of prefix c_pref at level c_lv
+    auto c_step = [&]() {
+        BinHit h;
+        if (!scan_bins<true>(hS, c_acc, T, lane, h)) {  // the candidates' whole mass stays below tau
+            c_found = false;
+            c_done = true;
+            return;
         }
-        if (c_on) {
-            // when the floor's candidates already hold tau of the mass, the
-            // TopCdf prefix is no longer than the floor
-            uint32_t m = 0;
-            for (int q = lane; 4 * q < nv; q += 64) {
-                const uint4 x = row4[q];
-                const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
-                    if (is_candidate(kk) && kk > x_pref) m += key_mass(kk);
-                }
-            }
-            m = wave_sum_u(m);
-            if (m + x_rem * key_mass(x_pref) >= T) c_on = false;
-        }
-    }
-    // TopCdf: the key at which the cumulative mass reaches tau
-    uint32_t c_pref = 0, c_cnt = 0;
-    if (c_on) {
-        uint32_t c_acc = 0;
-        bool found = true;
-        for (int lv = 0; lv < 4 && found; ++lv) {
-            digit_hist<true>(row4, nv, lv, c_pref, hS, lane);
-            uint32_t d = 0, bef = 0;
-            found = scan_digits(hS, c_acc, T, lane, d, bef);
-            c_acc += bef;
-            c_pref = (c_pref << digit_width(lv)) | d;
-        }
-        if (!found) {  // the candidates' whole mass stays below tau
-            k_cdf = n_cand;
-        } else {
-            // the key is shared by `grp` candidates of equal mass, taken in
-            // index order; `c_cnt` candidates rank above it
-            uint32_t above = 0, grp = 0;
-            for (int q = lane; 4 * q < nv; q += 64) {
-                const uint4 x = row4[q];
-                const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint32_t kk = 4 * q + t < nv ? xs[t] : 0u;
-                    above += (is_candidate(kk) && kk > c_pref) ? 1u : 0u;
-                    grp += kk == c_pref ? 1u : 0u;
-                }
-            }
-            c_cnt = wave_sum_u(above);
-            grp = wave_sum_u(grp);
+        c_acc += h.mass_before;
+        c_cnt += h.cnt_before;
+        c_pref = (c_pref << digit_width(c_lv)) | h.digit;
+        if (h.bin_cnt == 1u) {
+            c_thr = bin_floor(c_pref, c_lv);
+            c_quota = 0;
+            k_cdf = int(c_cnt + 1u);
+            c_done = true;
+        } else if (c_lv == 3) {
+            // the key is shared by bin_cnt candidates of equal mass, taken in index order
             const uint32_t Pv = key_mass(c_pref);
             const uint32_t need = T - c_acc;
-            uint32_t m = Pv ? (need - 1u) / Pv : grp - 1u;
-            m = min(m, grp - 1u);
+            uint32_t m = Pv ? (need - 1u) / Pv : h.bin_cnt - 1u;
+            m = min(m, h.bin_cnt - 1u);
+            c_thr = c_pref;
+            c_quota = m + 1u;
             k_cdf = int(c_cnt + m + 1u);
+            c_done = true;
         }
+        ++c_lv;
+    };
+    if (x_on) {
+        bool f_done = false;
+        for (int lv = 0; lv < 4 && !f_done; ++lv) {
+            digit_hist(row4, nv, lv, f_pref, hS, lane);
+            if (!c_done && c_lv == lv && c_pref == f_pref) c_step();
+            BinHit h;
+            scan_bins<false>(hS, 0u, f_rem, lane, h);
+            f_rem -= h.cnt_before;
+            f_mass += h.mass_before;
+            f_pref = (f_pref << digit_width(lv)) | h.digit;
+            if (h.bin_cnt == f_rem) {  // every candidate of the bin is needed
+                f_thr = bin_floor(f_pref, lv);
+                f_quota = 0;
+                f_mass += h.bin_mass;
+                f_done = true;
+            }
+        }
+        if (!f_done) {  // f_pref is the extra-th key; f_rem of its ties are needed
+            f_thr = f_pref;
+            f_quota = f_rem;
+            f_mass += f_rem * key_mass(f_pref);
+        }
+        // when the floor's candidates already hold tau of the mass, the TopCdf
+        // prefix is no longer than the floor
+        if (c_on && f_mass >= T) c_on = false;
+    }
+    if (c_on) {
+        while (!c_done) {
+            digit_hist(row4, nv, c_lv, c_pref, hS, lane);
+            c_step();
+        }
+        if (!c_found) k_cdf = n_cand;
+    } else if (T != 0u) {
+        k_cdf = 0;  // the floor already holds tau of the mass
     }
     const int keep = min(n_cand, max(k_cdf, extra));
 
@@ -566,11 +611,11 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
     } else if (keep == n_cand) {
         v_thr = 0u;  // every candidate passes
     } else if (keep == k_cdf) {
-        v_thr = c_pref;
-        quota = uint32_t(k_cdf) - c_cnt;
+        v_thr = c_thr;
+        quota = c_quota;
     } else {
-        v_thr = x_pref;
-        quota = x_rem;
+        v_thr = f_thr;
+        quota = f_quota;
     }
     uint8_t* out = a.mask + grow * a.n_kb;
     const bool aligned4 = (a.n_kb & 3) == 0;
@@ -618,9 +663,15 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
 }
 
 // Eight wavefronts per group of gr <= 16 query blocks; wavefront w selects query
-// blocks 2w and 2w+1.  Dynamic LDS: scores[16][ls] f32 | per wavefront:
-// histogram[256] u32 | column forcing bits[ceil(n_kb/32)] u32.
+// blocks 2w and 2w+1.  Dynamic LDS: scores[gr][ls] f32 | per selecting
+// wavefront: histogram[256] u64 | query-block means[16][D + 4] f32 | column
+// forcing bits[ceil(n_kb/32)] u32.
 constexpr int kTopcdfWaves = 8;
+// wavefronts that select rows (two each) and so hold a histogram
+__host__ __device__ constexpr int topcdf_sel_waves(int gr) { return (gr + 1) / 2; }
+// row stride (floats) of the query-block means in LDS: padded so that eight
+// consecutive rows start in different banks
+__host__ __device__ constexpr int topcdf_qrow(int d) { return d + 4; }
 
 template <int D>
 __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls, int gr) {
@@ -628,12 +679,14 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     __shared__ int32_t wave_tot[kTopcdfWaves];
     __shared__ float simq_g[kGroupRows];
     float* scores = reinterpret_cast<float*>(smem);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(scores + kGroupRows * ls);
-    uint32_t* colf = hist + kTopcdfWaves * 256;
+    unsigned long long* hist = reinterpret_cast<unsigned long long*>(scores + gr * ls);
+    float* qlds = reinterpret_cast<float*>(hist + topcdf_sel_waves(gr) * 256);
+    uint32_t* colf = reinterpret_cast<uint32_t*>(qlds + kGroupRows * topcdf_qrow(D));
 
     const int groups = (a.n_qb + gr - 1) / gr;
-    const int bh = blockIdx.x / groups;  // b * Hq + hq
-    const int i0 = (blockIdx.x - bh * groups) * gr;
+    const int g = blockIdx.x;
+    const int bh = g / groups;  // b * Hq + hq
+    const int i0 = (g - bh * groups) * gr;
     const int hq = bh % a.Hq;
     const int b = bh / a.Hq;
     const int hk = hq / (a.Hq / a.Hkv);
@@ -645,55 +698,84 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     const int i_last = min(i0 + gr, a.n_qb) - 1;
     const int ncols = row_geom(a, i_last).nv;  // columns any row of the group can see
 
-    // the group's query-block similarities, loaded once while the scores are computed
+    // Loads first, so their latencies overlap: the group's query-block means
+    // (one float4 per thread; rows past the group are zero), the key-block
+    // similarities for the column forcing, the group's query-block similarities.
+    constexpr int QROW = topcdf_qrow(D);
+    constexpr int QV4 = kGroupRows * D / 4;
+    static_assert(QV4 <= 64 * kTopcdfWaves, "one float4 of query means per thread");
+    const int qr = int(threadIdx.x) / (D / 4), qc4 = int(threadIdx.x) % (D / 4);
+    f32x4 qv = {0.f, 0.f, 0.f, 0.f};
+    if (int(threadIdx.x) < QV4 && qr < gr && i0 + qr < a.n_qb)
+        qv = *reinterpret_cast<const f32x4*>(a.qbar + (int64_t(bh) * a.n_qb + i0 + qr) * D + 4 * qc4);
+    // this wavefront's first tile of key-block means (see the score loop below)
+    constexpr int C = D / 16;
+    const int r16 = lane & 15;
+    const int sub = lane >> 4;
+    const int ntile = (ncols + 15) >> 4;
+    f32x4 kv[C];
+    auto load_tile = [&](int t) {
+        const float* ks = kbar + int64_t(min(t * 16 + r16, ncols - 1)) * D + 4 * sub;
+#pragma unroll
+        for (int c = 0; c < C; ++c) kv[c] = *reinterpret_cast<const f32x4*>(ks + 16 * c);
+    };
+    if (wave < ntile) load_tile(wave);
+    constexpr int kColSteps = (SA_MAX_KEY_BLOCKS + 64 * kTopcdfWaves - 1) / (64 * kTopcdfWaves);
+    float sk[kColSteps];
+#pragma unroll
+    for (int u = 0; u < kColSteps; ++u) {
+        const int j = 64 * (wave + kTopcdfWaves * u) + lane;
+        sk[u] = j < ncols ? simk[j] : 0.f;
+    }
     if (threadIdx.x < kGroupRows)
         simq_g[threadIdx.x] = a.simq[int64_t(bh) * a.n_qb + min(i0 + int(threadIdx.x), a.n_qb - 1)];
+    if (int(threadIdx.x) < QV4) *reinterpret_cast<f32x4*>(qlds + qr * QROW + 4 * qc4) = qv;
     // column forcing as bits: word j/32 of the mask, one ballot per 64 blocks
-    for (int j0 = 64 * wave; j0 < ncols; j0 += 64 * kTopcdfWaves) {
+#pragma unroll
+    for (int u = 0; u < kColSteps; ++u) {
+        const int j0 = 64 * (wave + kTopcdfWaves * u);
+        if (j0 >= ncols) break;
         const int j = j0 + lane;
-        const unsigned long long f = __ballot(j < ncols && column_forced(a, j, simk[j]));
+        const unsigned long long f = __ballot(j < ncols && column_forced(a, j, sk[u]));
         if (lane == 0) {
             colf[j0 >> 5] = uint32_t(f);
             colf[(j0 >> 5) + 1] = uint32_t(f >> 32);
         }
     }
+    __syncthreads();
 
     // ---- compressed scores on v_mfma_f32_16x16x4_f32: A = 16 key-block means
     // (rows), B = the group's 16 query-block means (columns).  Lane l feeds
     // operand slot l/16 of row/column l%16; head-dim entry 16c + 4(l/16) + e
     // goes to step (c, e), so each lane reads float4s of contiguous entries.
     // The result lands as query row l%16, key blocks 4(l/16)..+3 of the tile.
-    // One operand buffer per wavefront: 24 wavefronts per CU hide the loads.
-    {
-        constexpr int C = D / 16;
-        const int r16 = lane & 15;
-        const int sub = lane >> 4;
-        f32x4 qv[C];
-        const float* qs = a.qbar + (int64_t(bh) * a.n_qb + min(i0 + r16, a.n_qb - 1)) * D + 4 * sub;
+    // A wavefront takes every eighth tile.  The query operand is read from LDS
+    // at each step, which leaves the registers for all of a tile's key loads
+    // to be in flight at once.
+    for (int t = wave; t < ntile; t += kTopcdfWaves) {
+        // an opaque offset, so the query reads stay inside the loop
+        int qo = r16 * QROW + 4 * sub;
+        asm volatile("" : "+v"(qo));
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < C; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qs + 16 * c);
-        const int ntile = (ncols + 15) >> 4;
-        for (int t = wave; t < ntile; t += kTopcdfWaves) {
-            f32x4 kv[C];
-            const float* ks = kbar + int64_t(min(t * 16 + r16, ncols - 1)) * D + 4 * sub;
+        for (int c = 0; c < C; c += 2) {
+            const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlds + qo + 16 * c);
+            const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlds + qo + 16 * (c + 1));
 #pragma unroll
-            for (int c = 0; c < C; ++c) kv[c] = *reinterpret_cast<const f32x4*>(ks + 16 * c);
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < C; c += 2)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c][e], qv[c][e], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c + 1][e], qv[c + 1][e], acc1, 0, 0, 0);
-                }
-            const f32x4 sc = (acc0 + acc1) * a.scale;
-            // blocks past the row's room (the last tile's tail) are not stored
-            if (t * 16 + 4 * sub < ls) *reinterpret_cast<f32x4*>(scores + r16 * ls + t * 16 + 4 * sub) = sc;
+            for (int e = 0; e < 4; ++e) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c][e], q0[e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c + 1][e], q1[e], acc1, 0, 0, 0);
+            }
         }
+        if (t + kTopcdfWaves < ntile) load_tile(t + kTopcdfWaves);
+        const f32x4 sc = (acc0 + acc1) * a.scale;
+        // rows past the group and blocks past the row's room (the last tile's tail) are not stored
+        if (r16 < gr && t * 16 + 4 * sub < ls)
+            *reinterpret_cast<f32x4*>(scores + r16 * ls + t * 16 + 4 * sub) = sc;
     }
     __syncthreads();
 
-    uint32_t* hS = hist + wave * 256;
+    unsigned long long* hS = hist + wave * 256;
     int tot = 0;
     for (int rr = 2 * wave; rr < 2 * wave + 2; ++rr) {
         const int i = i0 + rr;
@@ -706,9 +788,9 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
         int sum = 0;
 #pragma unroll
         for (int w = 0; w < kTopcdfWaves; ++w) sum += wave_tot[w];
-        a.group_tot[blockIdx.x] = sum;
+        a.group_tot[g] = sum;
         // read only by the next launch: no ordering needed here
-        __hip_atomic_fetch_add(&a.super_tot[blockIdx.x / kSuperGroups], sum, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(&a.super_tot[g / kSuperGroups], sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -875,11 +957,12 @@ hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream) {
     if (a.n_kb > SA_MAX_KEY_BLOCKS) return hipErrorInvalidValue;
     const int ls = score_stride(a.n_kb);
     // column bits: whole 64-block ballots
-    const size_t lds = size_t(kGroupRows) * ls * 4 + size_t(kTopcdfWaves) * 256 * 4 + size_t(a.n_kb + 63) / 64 * 8;
+    const int gr = topcdf_group_rows(int64_t(a.B) * a.Hq, a.n_qb);
+    const size_t lds = size_t(gr) * ls * 4 + size_t(topcdf_sel_waves(gr)) * 256 * 8 +
+                       size_t(kGroupRows) * topcdf_qrow(a.D) * 4 + size_t(a.n_kb + 63) / 64 * 8;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t nwg = topcdf_groups(int64_t(a.B) * a.Hq, a.n_qb);
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
-    const int gr = topcdf_group_rows(int64_t(a.B) * a.Hq, a.n_qb);
     const dim3 block{64 * kTopcdfWaves, 1, 1};
     if (a.D == 128)
         hipLaunchKernelGGL(k_topcdf<128>, dim3(unsigned(nwg)), block, lds, stream, a, ls, gr);

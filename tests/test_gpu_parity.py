@@ -115,10 +115,10 @@ def host_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_path(w, sparsity="default"):
+def run_path(w, sparsity="default", inputs=None):
     cfg = sa.config_from_workload(w, sparsity)
     path = sa.SparseAttentionPath(cfg, forced=library_tile_pattern(w))
-    q, k, v = generate(w)
+    q, k, v = generate(w) if inputs is None else inputs
     mask = torch.zeros((cfg.rows, cfg.n_kb), dtype=torch.uint8, device="cuda")
     simq = torch.zeros(cfg.rows, dtype=torch.float32, device="cuda")
     simk = torch.zeros(cfg.B * cfg.Hkv * cfg.n_kb, dtype=torch.float32, device="cuda")
@@ -303,6 +303,54 @@ def test_dense_when_sparsity_zero():
             y, _ = OA.dense_attention(R.to_f64(q[b, h]), R.to_f64(k[b, h]), R.to_f64(v[b, h]))
             d = np.abs(o[b, h] - y)
             assert d.max() <= R.MAX_ABS and d.mean() <= R.MEAN_ABS
+
+
+@pytest.mark.parametrize("sparsity,tau", [(0.3, None), (0.7, None), (None, 0.5), (0.5, 0.9)])
+def test_exact_ties_rank_by_block_index(sparsity, tau):
+    """Key blocks that are bit-exact copies of one another tie exactly in probability, and
+    the selection ranks equal candidates by block index: among the candidate copies of one
+    block a row keeps the lowest indices first.  Every row must also be one the oracle
+    allows.  With five distinct blocks repeated across the row, the floor and TopCdf cuts
+    fall inside groups of copies."""
+    w = rep(SMALL["video_s"], theta=None, tau=tau, sparsity=sparsity)
+    q, k, v = generate(w)
+    perm, perm_k = R.oracle_perm(w), R.oracle_perm_k(w)
+    kp = np.take(k, perm_k, axis=2)
+    bk, Nk = w.block_k, kp.shape[2]
+    n_kb = -(-Nk // bk)
+    src = np.arange(n_kb) % 5
+    full = [j for j in range(n_kb) if (j + 1) * bk <= Nk]
+    for j in full:
+        if src[j] != j:
+            kp[:, :, j * bk:(j + 1) * bk] = kp[:, :, src[j] * bk:(src[j] + 1) * bk]
+    k2 = np.empty_like(k)
+    k2[:, :, perm_k] = kp
+    path, _, gmask, _, _ = run_path(w, inputs=(q, k2, v))
+    cfg = path.cfg
+    assert path.statuses()[0] == sa.SA_OK
+    mp = R.mask_params(w)
+    qp, kpf = R.permuted(q, perm), R.permuted(k2, perm_k)
+    split_groups = 0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = h // (w.Hq // w.Hkv)
+            ref = OP.predict_head(qp[b, h], kpf[b, hk], mp)
+            r0 = (b * w.Hq + h) * cfg.n_qb
+            bad, _, _, _ = R.compare_head_mask(gmask[r0:r0 + cfg.n_qb], ref, mp)
+            assert not bad, f"rows not admissible: {bad[:8]}"
+            for i in range(cfg.n_qb):
+                if ref["info"][i]["forced_row"]:
+                    continue
+                valid = OP._valid_blocks(i, mp)
+                cand = valid & ~OP._forced_blocks(i, mp, ref["simk"], valid)
+                row = gmask[r0 + i]
+                for g in range(5):
+                    members = [j for j in full if src[j] == g and cand[j]]
+                    kept = row[members]
+                    # kept copies come first in index order
+                    assert not np.any(~kept[:-1] & kept[1:]), (b, h, i, g, kept)
+                    split_groups += int(kept.any() and not kept.all())
+    assert split_groups > 0  # a cut fell inside a group of exact ties
 
 
 def test_permute_fp32_round_to_nearest_even():
