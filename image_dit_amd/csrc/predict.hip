@@ -349,9 +349,12 @@ constexpr uint32_t kForcedKey = 0x80000000u;
 __device__ inline uint32_t key_mass(uint32_t key) { return uint32_t(__uint_as_float(key - 1u) * kFix); }
 __device__ inline bool is_candidate(uint32_t key) { return key != 0u && key < kForcedKey; }
 
-// Radix digits of the keys: bits 29..22, 21..14, 13..6, 5..0.
-__device__ inline int digit_shift(int lv) { return lv == 3 ? 0 : 22 - 8 * lv; }
-__device__ inline int digit_width(int lv) { return lv == 3 ? 6 : 8; }
+// Radix digits of the keys: bits 29..23, 22..16, 15..9, 8..2, 1..0 (128-bin
+// histograms, so the histograms of a workgroup fit beside a long score row).
+constexpr int kLevels = 5;
+constexpr int kBins = 128;
+__device__ inline int digit_shift(int lv) { return lv == kLevels - 1 ? 0 : 23 - 7 * lv; }
+__device__ inline int digit_width(int lv) { return lv == kLevels - 1 ? 2 : 7; }
 
 // Histogram bins hold a count and a fixed-point mass together: count in the
 // high word, mass in the low word.  A bin's mass is a sum of candidate masses,
@@ -365,29 +368,28 @@ struct BinHit {
     uint32_t bin_mass;     // their mass
 };
 
-// In the histogram scan lane l owns digits 255-4l .. 252-4l (highest first).
+// In the histogram scan lane l owns digits 127-2l and 126-2l (highest first).
 // Finds the first digit, in descending order, at which base + the inclusive
 // cumulative mass (BY_MASS) or count reaches `target`; returns false when none
 // does.
 template <bool BY_MASS>
 __device__ inline bool scan_bins(const unsigned long long* hist, uint32_t base, uint32_t target, int lane,
                                  BinHit& h) {
-    const uint4* h4 = reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
-    const uint4 lo = h4[0], hi = h4[1];  // digits 252-4l, 253-4l | 254-4l, 255-4l
-    const uint32_t m[4] = {hi.z, hi.x, lo.z, lo.x};  // descending digits
-    const uint32_t c[4] = {hi.w, hi.y, lo.w, lo.y};
-    const uint32_t lm = m[0] + m[1] + m[2] + m[3];
-    const uint32_t lc = c[0] + c[1] + c[2] + c[3];
+    const uint4 h2 = *reinterpret_cast<const uint4*>(hist + kBins - 2 - 2 * lane);  // digits 126-2l, 127-2l
+    const uint32_t m[2] = {h2.z, h2.x};  // descending digits
+    const uint32_t c[2] = {h2.w, h2.y};
+    const uint32_t lm = m[0] + m[1];
+    const uint32_t lc = c[0] + c[1];
     const uint32_t im = wave_incl_scan(lm);
     const uint32_t ic = wave_incl_scan(lc);
     const unsigned long long hit = __ballot(base + (BY_MASS ? im : ic) >= target);
     if (hit == 0ull) return false;
     const int hl = __ffsll(static_cast<long long>(hit)) - 1;
     uint32_t rm = im - lm, rc = ic - lc;
-    uint32_t pos = 3, bm = rm, bc = rc, hm = m[3], hc = c[3];
+    uint32_t pos = 1, bm = rm, bc = rc, hm = m[1], hc = c[1];
     bool done = false;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
         if (!done && base + (BY_MASS ? rm + m[t] : rc + c[t]) >= target) {
             pos = t;
             bm = rm;
@@ -399,7 +401,7 @@ __device__ inline bool scan_bins(const unsigned long long* hist, uint32_t base, 
         rm += m[t];
         rc += c[t];
     }
-    h.digit = __builtin_amdgcn_readlane(255u - 4u * uint32_t(lane) - pos, hl);
+    h.digit = __builtin_amdgcn_readlane(uint32_t(kBins - 1) - 2u * uint32_t(lane) - pos, hl);
     h.cnt_before = __builtin_amdgcn_readlane(bc, hl);
     h.mass_before = __builtin_amdgcn_readlane(bm, hl);
     h.bin_cnt = __builtin_amdgcn_readlane(hc, hl);
@@ -408,13 +410,12 @@ __device__ inline bool scan_bins(const unsigned long long* hist, uint32_t base, 
 }
 
 // Histogram (count and mass per bin) of digit `lv` over the candidate keys
-// that carry prefix `pref` above it, in this wavefront's 256-bin LDS array.
+// that carry prefix `pref` above it, in this wavefront's kBins-bin LDS array.
 __device__ inline void digit_hist(const uint4* row4, int nv, int lv, uint32_t pref, unsigned long long* hist,
                                   int lane) {
     const int sh = digit_shift(lv), w = digit_width(lv);
     uint4* h4 = reinterpret_cast<uint4*>(hist);
-    h4[lane] = make_uint4(0, 0, 0, 0);
-    h4[lane + 64] = make_uint4(0, 0, 0, 0);
+    h4[lane] = make_uint4(0, 0, 0, 0);  // kBins / 2 uint4
     wave_lds_sync();
     for (int q = lane; 4 * q < nv; q += 64) {
         const uint4 x = row4[q];
@@ -445,7 +446,7 @@ __device__ inline uint32_t bin_floor(uint32_t pref, int lv) {
 // lane takes four consecutive key blocks per step.  Candidates are ordered by
 // probability descending, ties by block index ascending; TopCdf keeps the
 // shortest prefix whose mass reaches tau, the floor keeps at least `extra`
-// candidates.  Both cut points are found exactly with at most four histogram
+// candidates.  Both cut points are found exactly with at most five histogram
 // passes each over the radix digits of the keys, so no sort is needed.
 // Returns the row's kept count.
 __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint32_t* row, const uint32_t* colf,
@@ -554,7 +555,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
             c_quota = 0;
             k_cdf = int(c_cnt + 1u);
             c_done = true;
-        } else if (c_lv == 3) {
+        } else if (c_lv == kLevels - 1) {
             // the key is shared by bin_cnt candidates of equal mass, taken in index order
             const uint32_t Pv = key_mass(c_pref);
             const uint32_t need = T - c_acc;
@@ -569,7 +570,7 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
     };
     if (x_on) {
         bool f_done = false;
-        for (int lv = 0; lv < 4 && !f_done; ++lv) {
+        for (int lv = 0; lv < kLevels && !f_done; ++lv) {
             digit_hist(row4, nv, lv, f_pref, hS, lane);
             if (!c_done && c_lv == lv && c_pref == f_pref) c_step();
             BinHit h;
@@ -663,15 +664,21 @@ __device__ int select_row(const TopCdfArgs& a, int bh, int i, float simq_i, uint
 }
 
 // Eight wavefronts per group of gr <= 16 query blocks; wavefront w selects query
-// blocks 2w and 2w+1.  Dynamic LDS: scores[gr][ls] f32 | per selecting
-// wavefront: histogram[256] u64 | query-block means[16][D + 4] f32 | column
-// forcing bits[ceil(n_kb/32)] u32.
+// blocks 2w and 2w+1.  Dynamic LDS: scores[gr][ls] f32 | query-block
+// means[16][D + 4] f32 while the scores are computed, then per selecting
+// wavefront a histogram[kBins] u64 | column forcing bits[ceil(n_kb/32)] u32.
 constexpr int kTopcdfWaves = 8;
 // wavefronts that select rows (two each) and so hold a histogram
 __host__ __device__ constexpr int topcdf_sel_waves(int gr) { return (gr + 1) / 2; }
 // row stride (floats) of the query-block means in LDS: padded so that eight
 // consecutive rows start in different banks
 __host__ __device__ constexpr int topcdf_qrow(int d) { return d + 4; }
+// LDS bytes that hold the group's query-block means during the score products
+// and the selecting wavefronts' histograms after them
+__host__ __device__ constexpr int topcdf_union_bytes(int gr, int d) {
+    return topcdf_sel_waves(gr) * kBins * 8 > kGroupRows * topcdf_qrow(d) * 4 ? topcdf_sel_waves(gr) * kBins * 8
+                                                                             : kGroupRows * topcdf_qrow(d) * 4;
+}
 
 template <int D>
 __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int ls, int gr) {
@@ -680,8 +687,8 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     __shared__ float simq_g[kGroupRows];
     float* scores = reinterpret_cast<float*>(smem);
     unsigned long long* hist = reinterpret_cast<unsigned long long*>(scores + gr * ls);
-    float* qlds = reinterpret_cast<float*>(hist + topcdf_sel_waves(gr) * 256);
-    uint32_t* colf = reinterpret_cast<uint32_t*>(qlds + kGroupRows * topcdf_qrow(D));
+    float* qlds = reinterpret_cast<float*>(hist);  // the same bytes, dead once the score products are done
+    uint32_t* colf = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(hist) + topcdf_union_bytes(gr, D));
 
     const int groups = (a.n_qb + gr - 1) / gr;
     const int g = blockIdx.x;
@@ -775,7 +782,7 @@ __global__ __launch_bounds__(64 * kTopcdfWaves) void k_topcdf(TopCdfArgs a, int 
     }
     __syncthreads();
 
-    unsigned long long* hS = hist + wave * 256;
+    unsigned long long* hS = hist + wave * kBins;
     int tot = 0;
     for (int rr = 2 * wave; rr < 2 * wave + 2; ++rr) {
         const int i = i0 + rr;
@@ -958,8 +965,7 @@ hipError_t launch_topcdf(const TopCdfArgs& a, hipStream_t stream) {
     const int ls = score_stride(a.n_kb);
     // column bits: whole 64-block ballots
     const int gr = topcdf_group_rows(int64_t(a.B) * a.Hq, a.n_qb);
-    const size_t lds = size_t(gr) * ls * 4 + size_t(topcdf_sel_waves(gr)) * 256 * 8 +
-                       size_t(kGroupRows) * topcdf_qrow(a.D) * 4 + size_t(a.n_kb + 63) / 64 * 8;
+    const size_t lds = size_t(gr) * ls * 4 + topcdf_union_bytes(gr, a.D) + size_t(a.n_kb + 63) / 64 * 8;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t nwg = topcdf_groups(int64_t(a.B) * a.Hq, a.n_qb);
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
