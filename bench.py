@@ -57,7 +57,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the attention kernel needs about ten dispatches before its clock settles
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--sparsity", type=float, default=None, help="override the workload's sparsity")
     ap.add_argument("--mode", default="path", choices=["path", "attn", "predict", "reorder", "copy", "ceilings"])
