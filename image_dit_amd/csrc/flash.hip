@@ -30,6 +30,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// An exp2 argument below this gives 0 in fp32 (the smallest subnormal is 2^-149),
+// with a wide margin for the rounding of the argument.
+constexpr float kExpZeroArg = -200.0f;
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -976,7 +979,8 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             }
             float lo, hi;
             swap32(max3f(mx[0], mx[1], max2f(mx[2], mx[3])), lo, hi);
-            const float smax = max2f(lo, hi) * f;
+            const float smax_raw = max2f(lo, hi);  // the row's largest score of this tile
+            const float smax = smax_raw * f;
             const float m_new = max2f(m_run, smax);
             // the block's row maximum: this tile's, or (second half) both halves'
             const float bmax = second ? max2f(mx_first, smax) : smax;
@@ -986,32 +990,41 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             alpha = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;  // 0 when m_run = -inf
             m_run = m_new;
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
-            if constexpr (!FP8) {
-                // every exponent argument first, in place, then the exponentials: no
-                // instruction waits on the one just before it (measured faster for bf16
-                // scores, slower for the shorter FP8 score phase)
+            // A skipped tile whose largest exponent argument (the same fma as below, on
+            // the row's largest score) lies under -200 for every row has exp2 = 0 for
+            // all its scores: its P and row-sum terms are exactly 0 and alpha is 1 (the
+            // maximum did not move), so the exponentials are left out with no change to
+            // any result.  NaN scores take the full path.
+            const bool zero = !first && skip &&
+                              __builtin_amdgcn_ballot_w64(row_valid && !(fmaf(smax_raw, c2t, -mc) < kExpZeroArg)) == 0ull;
+            if (!zero) {
+                if constexpr (!FP8) {
+                    // every exponent argument first, in place, then the exponentials: no
+                    // instruction waits on the one just before it (measured faster for bf16
+                    // scores, slower for the shorter FP8 score phase)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s0[i] = fmaf(s0[i], c2t, -mc);
-                    s1[i] = fmaf(s1[i], c2t, -mc);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < 16; ++i) {
+                        s0[i] = fmaf(s0[i], c2t, -mc);
+                        s1[i] = fmaf(s1[i], c2t, -mc);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s0[i] = __builtin_amdgcn_exp2f(s0[i]);
-                    s1[i] = __builtin_amdgcn_exp2f(s1[i]);
-                }
-            } else {
+                    for (int i = 0; i < 16; ++i) {
+                        s0[i] = __builtin_amdgcn_exp2f(s0[i]);
+                        s1[i] = __builtin_amdgcn_exp2f(s1[i]);
+                    }
+                } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
-                    s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
+                    for (int i = 0; i < 16; ++i) {
+                        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2t, -mc));
+                        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2t, -mc));
+                    }
                 }
+                float ps[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
+                l_part = fmaf(l_part, alpha, ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
             }
-            float ps[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ps[i] = (s0[2 * i] + s0[2 * i + 1]) + (s1[2 * i] + s1[2 * i + 1]);
-            l_part = fmaf(l_part, alpha, ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
             if (first) {
                 my_need = 1;  // undecided: kept pending until the second half decides
             } else if (skip) {
