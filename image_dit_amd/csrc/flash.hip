@@ -990,13 +990,18 @@ void k_flash_lam(FlashArgs a, const int32_t* __restrict__ row_ptr, const int32_t
             alpha = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;  // 0 when m_run = -inf
             m_run = m_new;
             const float mc = (m_new == -INFINITY ? 0.f : m_new) * c2;
-            // A skipped tile whose largest exponent argument (the same fma as below, on
-            // the row's largest score) lies under -200 for every row has exp2 = 0 for
-            // all its scores: its P and row-sum terms are exactly 0 and alpha is 1 (the
-            // maximum did not move), so the exponentials are left out with no change to
-            // any result.  NaN scores take the full path.
-            const bool zero = !first && skip &&
-                              __builtin_amdgcn_ballot_w64(row_valid && !(fmaf(smax_raw, c2t, -mc) < kExpZeroArg)) == 0ull;
+            // A skipped tile leaves alpha at 1 (the maximum did not move) and needs no P,
+            // so all it does is add its exponentials to the row sum.  With `arg` the
+            // largest exponent argument (the same fma as below, on the row's largest
+            // score), a lane adds at most 32 * 2^arg to its l_part: nothing when arg is
+            // under -200 (every exp2 is 0), and nothing after rounding when that bound
+            // is under half an ulp of l_part (l_part in [2^(E-1), 2^E): arg < E - 31,
+            // one step of margin).  When that holds on every row the exponentials are
+            // left out, with no change to any result.  NaN scores take the full path.
+            const float arg = fmaf(smax_raw, c2t, -mc);
+            const bool lost = arg < kExpZeroArg ||
+                              (l_part > 0.f && arg < float(__builtin_amdgcn_frexp_expf(l_part) - 31));
+            const bool zero = !first && skip && __builtin_amdgcn_ballot_w64(row_valid && !lost) == 0ull;
             if (!zero) {
                 if constexpr (!FP8) {
                     // every exponent argument first, in place, then the exponentials: no
